@@ -1,0 +1,206 @@
+"""Benchmark of the paged-decode hot path on one MI355X.
+
+A step is one decode step of the 70B-style GQA model the pages size (80 layers,
+8 KV heads of 128 dims, bf16): for each of 80 layers, the new tokens' K/V are
+scattered into that layer's paged pool (reshape_and_cache) and paged decode
+attention runs over it.  Each layer has its own pool of 2,457 blocks (the
+12 GiB budget of the pages split over 80 layers), so a step streams about
+12.7 GB of KV and repeats never hit in the 256 MB last-level cache.
+
+value = KV bytes a step must read (sum over sequences of context_len x 2 x
+h_kv x head_dim x 2 B, x 80 layers) / step time, in GB/s.
+roofline = the decode kernel alone: the same bytes per launch / its average
+launch duration (HIP events around each launch, on its stream).
+cpu_baseline = the float64 oracle on a bounded sample of one layer.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak), seqs/s at 1 GPU"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "gqa70b-bf16-47x825"
+
+
+def kv_bytes_per_call(plan, unique=True):
+    """Algorithmic K+V bytes one decode call reads: used tokens only."""
+    import workloads
+    wl = plan.workload
+    per_token = 2 * wl.h_kv * wl.head_dim * workloads.ELEMENT_BYTES[wl.kv_dtype]
+    total = int(plan.context_lens.astype("int64").sum()) * per_token
+    if unique and wl.layout == "shared_prefix":
+        groups = -(-wl.num_seqs // wl.group_size)
+        total -= (wl.num_seqs - groups) * wl.prefix_tokens * per_token
+    return total
+
+
+def cpu_baseline(plan, rp, tensors, budget_s):
+    """Time the oracle (scatter + attention, one sequence at a time) on as many
+    sequences of one layer as fit in about budget_s seconds."""
+    import numpy as np
+    import torch
+
+    import oracle.attention
+    import oracle.scatter
+
+    wl = plan.workload
+    bits = {torch.float32: (torch.int32, np.uint32), torch.float16: (torch.int16, np.uint16),
+            torch.bfloat16: (torch.int16, np.uint16), torch.uint8: (torch.uint8, np.uint8)}
+    to_np = lambda x: x.view(bits[x.dtype][0]).cpu().numpy().view(bits[x.dtype][1])
+    q, kc, vc = to_np(tensors.q), to_np(tensors.k_cache), to_np(tensors.v_cache)
+    nk, nv = to_np(tensors.new_k), to_np(tensors.new_v)
+    per_token = 2 * wl.h_kv * wl.head_dim * {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    t0 = time.perf_counter()
+    kc2, vc2 = oracle.scatter.reshape_and_cache(nk, nv, kc, vc, rp.slot_mapping, in_dtype=wl.new_dtype,
+                                                kv_dtype=wl.kv_dtype, block_size=wl.block_size,
+                                                k_scale=tensors.k_scale, v_scale=tensors.v_scale)
+    done_bytes, done_seqs = 0, 0
+    for s in range(wl.num_seqs):
+        oracle.attention.paged_attention_decode(q, kc2, vc2, rp.block_tables, plan.context_lens, q_dtype=wl.q_dtype,
+                                                kv_dtype=wl.kv_dtype, block_size=wl.block_size,
+                                                scale=1.0 / math.sqrt(wl.head_dim), k_scale=tensors.k_scale,
+                                                v_scale=tensors.v_scale, seqs=[s])
+        done_seqs += 1
+        done_bytes += int(plan.context_lens[s]) * per_token
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "seqs_per_s": round(done_seqs / dt, 3), "host_cpus": os.cpu_count(),
+            "sample": f"{done_seqs} of {wl.num_seqs} sequences of one layer of {wl.name} "
+                      f"(scatter of all new tokens + float64 attention, one sequence at a time), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--layers", type=int, default=80)
+    ap.add_argument("--splits", type=int, default=0, help="force the decode split count (0 = library's choice)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_431_amd as pkv
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    wl = workloads.get(args.workload)
+    plan = workloads.plan(wl)
+    bm = pkv.BlockManager(plan.num_blocks, wl.block_size, plan.free_order)
+    rp = workloads.replay(plan, bm)
+    L = args.layers
+    pools = [workloads.make_tensors(plan, rp, device=dev, poison=False, pool_seed_offset=l) for l in range(L)]
+    tables = torch.from_numpy(rp.block_tables).to(dev)
+    lens = torch.from_numpy(plan.context_lens).to(dev)
+    slots = torch.from_numpy(rp.slot_mapping).to(dev)
+    out = torch.empty(wl.num_seqs, wl.h_q, wl.head_dim, dtype=torch.float32, device=dev)
+    ws = pkv.make_workspace(wl.num_seqs, wl.h_q, wl.h_kv, wl.head_dim, wl.block_size, plan.max_context_len,
+                            args.splits, device=dev)
+    n_splits = pkv.pkv_decode_num_splits(wl.num_seqs, wl.h_q, wl.h_kv, wl.head_dim, wl.block_size,
+                                         plan.max_context_len, args.splits)
+    stream = torch.cuda.current_stream()
+
+    # Validate and marshal every launch once; the timed loop only issues them.
+    decodes = [pkv.prepare_paged_attention_decode(out, t.q, t.k_cache, t.v_cache, tables, lens,
+                                                  max_context_len=plan.max_context_len, k_scale=t.k_scale,
+                                                  v_scale=t.v_scale, num_splits=args.splits, workspace=ws,
+                                                  stream=stream) for t in pools]
+    scatters = [pkv.prepare_reshape_and_cache(t.new_k, t.new_v, t.k_cache, t.v_cache, slots, k_scale=t.k_scale,
+                                              v_scale=t.v_scale, stream=stream) for t in pools]
+    layer_calls = list(zip(scatters, decodes))
+
+    def step():
+        for scatter, decode in layer_calls:
+            scatter()
+            decode()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # The decode kernel alone: an event pair around every launch.
+    reps = max(1, min(5, args.steps))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * L)]
+    for r in range(reps):
+        for l, decode in enumerate(decodes):
+            a, b = evs[r * L + l]
+            a.record(stream)
+            decode()
+            b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    mean_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    per_call = kv_bytes_per_call(plan)
+    step_bytes = per_call * L
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = per_call / (mean_launch_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q; block tables from the block manager over a shuffled free list)",
+        "config": {"workload": wl.name, "layers": L, "num_seqs": wl.num_seqs,
+                   "context_lens": "825 each" if len(set(plan.context_lens.tolist())) == 1 else "mixed",
+                   "max_context_len": plan.max_context_len, "h_q": wl.h_q, "h_kv": wl.h_kv,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
+                   "q_dtype": wl.q_dtype, "pool_blocks_per_layer": plan.num_blocks, "num_splits": n_splits,
+                   "kv_bytes_per_layer_call": per_call, "kv_bytes_per_step": step_bytes},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(wl.num_seqs / (ms_step * 1e-3 / L), 1),
+        "decode_steps_per_s": round(1000.0 / ms_step, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_mfma_kernel" if wl.kv_dtype != "f32" else "decode_vector_kernel",
+                     "mean_launch_us": round(mean_launch_ms * 1e3, 3),
+                     "median_launch_us": round(launch_ms[len(launch_ms) // 2] * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        del pools, decodes, scatters, layer_calls
+        torch.cuda.empty_cache()
+        fresh = workloads.make_tensors(plan, rp, device=dev, poison=False, pool_seed_offset=0)  # untouched by HIP
+        result["cpu_baseline"] = cpu_baseline(plan, rp, fresh, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

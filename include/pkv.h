@@ -1,0 +1,218 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged KV-cache decode attention for MI355X (gfx950).
+ *
+ * What the library computes
+ *   The KV cache of every sequence is cut into fixed-size blocks of
+ *   block_size tokens that may sit anywhere in a pool; a per-sequence block
+ *   table maps logical block j to its physical block ("AI Engineering
+ *   Visualised: KV cache", intro; "KV cache and PagedAttention in serving",
+ *   section "PagedAttention: virtual memory for GPUs").  The attention
+ *   kernel computes attention directly over those blocks through the block
+ *   table, never gathering them into a contiguous copy (same section; "Paged
+ *   KV Cache" tutorial, section "Block Tables and Sharing").  Decode attends
+ *   one new query token per sequence over the cached K/V of the tokens
+ *   processed so far ("KV cache and PagedAttention in serving", section
+ *   "What the KV cache actually is").
+ *
+ *   Attention here is softmax(scale * q . K^T) . V per query head, scale
+ *   defaulting to 1/sqrt(head_dim); query head g reads KV head
+ *   g / (h_q / h_kv) (grouped-query attention, "Paged KV Cache" tutorial,
+ *   section "Reproduce Bytes per Token": query heads share KV heads).
+ *
+ * Conventions for every entry point
+ *   - All tensors are dense, row-major, in device memory owned by the caller.
+ *     The library allocates no device memory and keeps no pointer after a
+ *     call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *     stream).  Buffers must stay valid until the stream has passed the call.
+ *     No call synchronizes the stream.
+ *   - The return value is a pkv_status; nothing throws across the ABI.
+ *     Scalar arguments are validated before anything is launched; on error
+ *     nothing is launched and no memory is touched.
+ *   - Device-resident data (block ids, context lengths, slots) is not read
+ *     by the host.  The kernels bound every access: a block id outside
+ *     [0, num_blocks) or a slot outside the pool is skipped rather than
+ *     followed, and a context length is clamped to
+ *     [0, max_blocks_per_seq * block_size].  Such inputs give undefined
+ *     numbers, never an out-of-bounds access.
+ *   - Thread-safe: the only global state is read-only after first use.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types a tensor can hold. */
+typedef enum {
+  PKV_F32 = 0,      /* IEEE binary32 */
+  PKV_F16 = 1,      /* IEEE binary16 */
+  PKV_BF16 = 2,     /* bfloat16: the upper half of a binary32 */
+  PKV_FP8_E4M3 = 3  /* OCP E4M3 (no infinities, max 448), one fp32 scale per tensor */
+} pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* a scalar argument is out of range or a pointer is NULL */
+  PKV_EUNSUPPORTED = 2,  /* valid, but this dtype / head_dim / group combination is not built */
+  PKV_ENOSPC = 3,        /* block manager: the pool cannot supply the blocks (state unchanged) */
+  PKV_EWORKSPACE = 4,    /* workspace smaller than pkv_decode_workspace_bytes() */
+  PKV_EHIP = 5           /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+/* Human-readable name of a status code (static string). */
+const char* pkv_status_str(int status);
+
+/* ABI version of this header (bumped on any signature change). */
+#define PKV_ABI_VERSION 1
+int pkv_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention
+ *
+ * Shapes (S = num_seqs, Hq = h_q, Hkv = h_kv, D = head_dim, B = block_size,
+ * NB = num_blocks, MB = max_blocks_per_seq):
+ *   out          [S, Hq, D]       out_dtype in {F32, F16, BF16}
+ *   q            [S, Hq, D]       q_dtype in {F32, F16, BF16}
+ *   k_cache      [NB, Hkv, B, D]  kv_dtype
+ *   v_cache      [NB, Hkv, B, D]  kv_dtype
+ *   block_tables [S, MB] int32    physical block of logical block j of seq s;
+ *                                  entries j >= ceil(ctx_s / B) are never read
+ *   context_lens [S] int32        ctx_s: tokens attended by seq s; positions
+ *                                  t >= ctx_s are never read (their bytes may
+ *                                  be anything, NaN included)
+ * Semantics: for each seq s and query head g (kv head h = g / (Hq / Hkv)):
+ *   out[s, g, :] = sum_t softmax_t(scale * q[s, g, :] . K_s[h, t, :]) V_s[h, t, :]
+ * over t in [0, ctx_s), where K_s[h, t, :] = k_cache[block_tables[s, t / B],
+ * h, t % B, :] (times k_scale for FP8) and likewise for V.  ctx_s = 0 gives 0.
+ *
+ * Supported combinations (others return PKV_EUNSUPPORTED):
+ *   D in {64, 128}; 1 <= Hq / Hkv <= 16; B >= 1;
+ *   (q, kv) in {(F32, F32), (F16, F16), (BF16, BF16), (BF16, FP8_E4M3),
+ *   (F16, FP8_E4M3)}.  The matrix-core path serves the 16-bit and FP8 caches
+ *   when B is a multiple of 16; everything else takes the vector path.
+ *
+ * max_context_len: an upper bound the host knows for max_s ctx_s (used only
+ *   to size the split over blocks; a longer ctx_s is still computed exactly).
+ * scale: logit scale; pass 0 (or a negative value) for 1/sqrt(D).
+ * k_scale, v_scale: per-tensor FP8 scales (ignored for other kv dtypes).
+ * num_splits: 0 lets the library choose how many workgroups share one
+ *   sequence's blocks; a positive value forces that count (tests, tuning).
+ *
+ * Workspace: device memory of at least pkv_decode_workspace_bytes(...) bytes
+ *   for the same (S, Hq, Hkv, D, max_context_len, num_splits).  It must be
+ *   zero-filled before its FIRST use; every call leaves it ready for the next
+ *   (its counters return to zero), so it is reused without clearing.  Two
+ *   calls in flight at once must not share a workspace.
+ *   Errors: PKV_EINVAL (NULL pointer, S < 0, Hq % Hkv != 0, B < 1,
+ *   max_context_len > MB * B, ...), PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP.
+ * ------------------------------------------------------------------------ */
+size_t pkv_decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                                  int max_context_len, int num_splits);
+
+/* The split count the library will use for these sizes (>= 1), or 0 if invalid. */
+int pkv_decode_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                          int max_context_len, int num_splits);
+
+int pkv_paged_attention_decode(void* out, int out_dtype,
+                               const void* q, int q_dtype,
+                               const void* k_cache, const void* v_cache, int kv_dtype,
+                               float k_scale, float v_scale,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                               int num_blocks, int max_blocks_per_seq, int max_context_len,
+                               float scale, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * reshape_and_cache: write each new token's K and V into its slot.
+ *
+ * A slot is physical_block * block_size + offset_in_block; token i's K for
+ * KV head h lands at k_cache[slot_i / B, h, slot_i % B, :] (same for V).  A
+ * sequence grows by claiming free blocks without moving earlier ones ("Paged
+ * KV Cache" tutorial, section "Answer Key", question 2), so a new token only
+ * ever writes its own slot.
+ *   key, value    [T, Hkv, D] in in_dtype (T = num_tokens)
+ *   slot_mapping  [T] int64; slot < 0 marks padding (skipped); a slot outside
+ *                 [0, NB * B) is skipped too.  Two tokens must not share a slot.
+ *   k_cache ...   [NB, Hkv, B, D] in kv_dtype
+ * Conversion: in_dtype == kv_dtype copies the bits; kv_dtype FP8_E4M3 takes
+ *   in_dtype F32 / F16 / BF16 and stores round-to-nearest-even(x / scale) with
+ *   one correctly rounded binary32 division, saturating to +-448, NaN -> 0x7F.
+ * D must be a multiple of 8.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
+ * ------------------------------------------------------------------------ */
+int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype,
+                          void* k_cache, void* v_cache, int kv_dtype,
+                          float k_scale, float v_scale,
+                          const int64_t* slot_mapping, int num_tokens,
+                          int h_kv, int head_dim, int block_size, int num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block manager (no device memory; pure host bookkeeping)
+ *
+ * Blocks are handed out only as a sequence grows ("AI Engineering
+ * Visualised: KV cache", intro), one free block at a time with no relocation
+ * of earlier blocks ("Paged KV Cache" tutorial, "Answer Key", question 2); a
+ * block returns to the free list once nothing references it, and sequences
+ * share prefix blocks by reference count with copy-on-write when they
+ * diverge inside a shared tail block (same tutorial, "Block Tables and
+ * Sharing"; "KV cache and PagedAttention in serving", "The bonus: sharing
+ * via copy-on-write").
+ *
+ * Policy: the free list is FIFO (take from the front, released blocks go to
+ * the back, a freed sequence releases in block-table order), seeded by
+ * `free_order` (a permutation of [0, num_blocks); NULL means ascending).
+ * Sequence ids are any non-negative int32.  Not thread-safe per manager.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_bm pkv_bm;
+
+/* Create a manager; *out receives it.  PKV_EINVAL on bad sizes or a
+ * free_order that is not a permutation. */
+int pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pkv_bm** out);
+void pkv_bm_destroy(pkv_bm* bm);
+
+/* Append n_tokens tokens to seq (created empty if new).  slots_out (may be
+ * NULL) receives the n_tokens slots in order.  If the sequence's last block
+ * is partly filled and shared, the sequence first moves to a fresh block:
+ * *cow_src / *cow_dst (may be NULL) receive the old and new block ids and
+ * the caller must copy the filled slots of src into dst; otherwise both are
+ * -1.  PKV_ENOSPC if the pool cannot supply every block needed (nothing
+ * changes); PKV_EINVAL for seq < 0 or n_tokens < 0. */
+int pkv_bm_append(pkv_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                  int32_t* cow_src, int32_t* cow_dst);
+
+/* child becomes a copy of parent sharing all its blocks (refcounts + 1).
+ * PKV_EINVAL if parent is unknown or child exists. */
+int pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child);
+
+/* Drop seq; blocks whose refcount reaches zero go to the back of the free
+ * list in block-table order.  PKV_EINVAL if seq is unknown. */
+int pkv_bm_free(pkv_bm* bm, int32_t seq);
+
+/* Copy seq's block table (up to cap entries) into out; *n_blocks and
+ * *n_tokens receive its length in blocks and tokens.  PKV_EINVAL if unknown
+ * or cap is too small. */
+int pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t cap,
+                       int32_t* n_blocks, int32_t* n_tokens);
+
+/* Fill the device-bound metadata of a batch: tables [num_seqs, max_blocks]
+ * (unused entries -1) and context_lens [num_seqs] for the listed sequences.
+ * PKV_EINVAL if a sequence is unknown or longer than max_blocks blocks. */
+int pkv_bm_export(const pkv_bm* bm, const int32_t* seqs, int32_t num_seqs,
+                  int32_t* tables, int32_t max_blocks, int32_t* context_lens);
+
+int32_t pkv_bm_num_free(const pkv_bm* bm);
+/* Reference count of a block (0 = free), or -1 for an id outside the pool. */
+int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
+/* Copy the free list, front first (up to cap entries); *n receives its length. */
+int pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

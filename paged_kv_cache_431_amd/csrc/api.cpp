@@ -1,0 +1,165 @@
+// C ABI of libpkv: argument validation, work-split choice and kernel dispatch.
+// The declarations in include/pkv.h document every entry point.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+// Workgroups of the decode kernel resident at once on an MI355X: 256 compute
+// units, 3 four-wave workgroups each (the matrix-core kernel's register use
+// allows 3 waves per SIMD).  Only used to size the split over blocks.
+constexpr int64_t kResidentWorkgroups = 256 * 3;
+
+bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of workgroups that share one (sequence, KV head): minimise
+// (rounds of resident workgroups) x (per-workgroup time), with the time of a
+// workgroup counted in tiles per wave plus a fixed cost for its prologue and
+// epilogue and one more tile's worth for the cross-split merge.
+int choose_splits(int64_t units, int64_t max_tiles) {
+  if (max_tiles <= 1 || units <= 0) return 1;
+  const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(max_tiles, 8)));
+  const int64_t padded_units = ceil_div(units, 8) * 8;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int64_t n = 1; n <= cap; ++n) {
+    const int64_t rounds = ceil_div(padded_units * n, kResidentWorkgroups);
+    const int64_t per_wave = ceil_div(ceil_div(max_tiles, n), pkv::kDecodeWaves);
+    const int64_t cost = rounds * (per_wave + 2 + (n > 1 ? 1 : 0));
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = (int)n;
+    }
+  }
+  return best;
+}
+
+int resolve_splits(int num_seqs, int h_kv, int max_context_len, int num_splits) {
+  const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
+  int n = num_splits > 0 ? num_splits : choose_splits((int64_t)num_seqs * h_kv, max_tiles);
+  return std::max(1, n);
+}
+
+bool decode_shape_ok(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_context_len,
+                     int num_splits) {
+  return num_seqs >= 0 && h_q >= 1 && h_kv >= 1 && h_q % h_kv == 0 && head_dim >= 1 && block_size >= 1 &&
+         max_context_len >= 0 && num_splits >= 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_str(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_EINVAL: return "PKV_EINVAL: invalid argument";
+    case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED: combination not built";
+    case PKV_ENOSPC: return "PKV_ENOSPC: not enough free blocks";
+    case PKV_EWORKSPACE: return "PKV_EWORKSPACE: workspace too small";
+    case PKV_EHIP: return "PKV_EHIP: HIP runtime error";
+    default: return "unknown pkv status";
+  }
+}
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+int pkv_decode_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_context_len,
+                          int num_splits) {
+  if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return 0;
+  return resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
+}
+
+size_t pkv_decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                                  int max_context_len, int num_splits) {
+  if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return 0;
+  const int n = resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
+  return pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n).total;
+}
+
+int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+                               const void* v_cache, int kv_dtype, float k_scale, float v_scale,
+                               const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q,
+                               int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                               int max_context_len, float scale, int num_splits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return PKV_EINVAL;
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return PKV_EINVAL;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_EINVAL;
+  if (!valid_dtype(out_dtype) || !valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace) return PKV_EINVAL;
+  if (!(std::isfinite(scale))) return PKV_EINVAL;
+  if (kv_dtype == PKV_FP8_E4M3 && !(k_scale > 0.f && std::isfinite(k_scale) && v_scale > 0.f && std::isfinite(v_scale)))
+    return PKV_EINVAL;
+
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if (h_q / h_kv > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
+  if (out_dtype == PKV_FP8_E4M3 || q_dtype == PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
+  const bool pair_ok = (q_dtype == kv_dtype) || (kv_dtype == PKV_FP8_E4M3 && q_dtype != PKV_F32);
+  if (!pair_ok) return PKV_EUNSUPPORTED;
+
+  const int n = resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
+  const pkv::WorkspaceLayout L = pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n);
+  if (workspace_bytes < L.total) return PKV_EWORKSPACE;
+
+  const double s = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)head_dim);
+  const double log2e = 1.4426950408889634;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+
+  pkv::DecodeLaunch a;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_dtype = kv_dtype;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_splits = n;
+  a.tiles_per_split = (int)std::max<int64_t>(1, ceil_div(ceil_div(max_context_len, pkv::kTileTokens), n));
+  a.scale_log2 = (float)(s * log2e * (fp8 ? (double)k_scale : 1.0));
+  a.v_scale = fp8 ? v_scale : 1.f;
+  a.workspace = workspace;
+  a.matrix_core = kv_dtype != PKV_F32 && block_size % pkv::kTileTokens == 0;
+  const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype, void* k_cache, void* v_cache,
+                          int kv_dtype, float k_scale, float v_scale, const int64_t* slot_mapping, int num_tokens,
+                          int h_kv, int head_dim, int block_size, int num_blocks, void* stream) {
+  if (num_tokens < 0 || h_kv < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1) return PKV_EINVAL;
+  if (!valid_dtype(in_dtype) || !valid_dtype(kv_dtype)) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_EINVAL;
+  if (kv_dtype == PKV_FP8_E4M3 && in_dtype != PKV_FP8_E4M3 &&
+      !(k_scale > 0.f && std::isfinite(k_scale) && v_scale > 0.f && std::isfinite(v_scale)))
+    return PKV_EINVAL;
+  if (head_dim % 8 != 0) return PKV_EUNSUPPORTED;
+  if (in_dtype != kv_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
+  const hipError_t e =
+      pkv::launch_reshape_and_cache(key, value, in_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, slot_mapping,
+                                    num_tokens, h_kv, head_dim, block_size, num_blocks,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // extern "C"

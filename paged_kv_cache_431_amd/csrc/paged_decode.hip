@@ -1,0 +1,663 @@
+// Paged decode attention for gfx950 (MI355X).
+//
+// The attention of one new query token per sequence over that sequence's
+// cached K/V, read block by block through the sequence's block table, never
+// gathered into a contiguous copy ("KV cache and PagedAttention in serving",
+// section "PagedAttention: virtual memory for GPUs"; "Paged KV Cache"
+// tutorial, section "Block Tables and Sharing").  Query head g reads KV head
+// g / G with G = h_q / h_kv, so one workgroup serves the whole query group of
+// a KV head and reads each K/V byte once.
+//
+// Work decomposition
+//   One workgroup (4 waves) per (sequence, KV head, split).  The sequence's
+//   16-token tiles are cut into `n` contiguous ranges (n <= num_splits, chosen
+//   per sequence on the device from its own length); within a range, wave w
+//   takes tiles w, w+4, w+8, ...  Each wave keeps an online-softmax state
+//   (running max m, running sum l, unnormalised output acc) per query row; the
+//   4 waves merge through LDS; a sequence with several ranges writes partial
+//   states to the workspace and the last workgroup to finish (an atomic
+//   counter per (sequence, KV head)) merges them and writes the output, so a
+//   call is a single kernel launch.
+//
+// Matrix-core path (16-bit or FP8 caches, block_size a multiple of 16)
+//   Scores: S^T[token][g] = K[token][:] . Q[g][:] with v_mfma_f32_16x16x32
+//   (bf16 or f16): K is the A operand and is loaded straight from HBM in the
+//   operand layout (lane = token, 16-byte chunks of the row), Q (padded to 16
+//   rows) is the B operand and stays in registers for the whole walk.  The
+//   accumulator layout puts scores for tokens 4*(lane/16)+r of query row
+//   lane%16 in lane `lane`, which is exactly the B-operand layout the PV
+//   product needs, so probabilities never move between lanes.
+//   PV: O^T[d][g] += V^T[d][token] P^T[token][g].  The contraction index is
+//   the token, so V must be transposed: each lane loads 4 token rows of an
+//   8-element d-chunk with coalesced 16-byte loads, packs the 4 tokens of each
+//   d into 8 bytes and stores them into a per-wave LDS tile [d][token]
+//   (rows XOR-swizzled to spread banks); the MFMA A operand is then one
+//   8-byte LDS read per 16-row output tile.  The probabilities are split into
+//   a hi and a lo 16-bit part (p = hi + lo + O(2^-16 p)) carried in the upper
+//   and lower halves of the MFMA's K = 32 (V is duplicated in the A operand),
+//   so one instruction applies both and P keeps ~16 bits of precision.
+//   FP8 (OCP E4M3) K/V are converted in registers by the hardware converter
+//   (exact into bf16/f16); k_scale folds into the logit scale and v_scale
+//   into the final normalisation.
+//   Tokens past the context (the tail of the last block) are masked by select,
+//   never by multiplying, so whatever those slots hold (NaN included) cannot
+//   leak into the result.
+//
+// Vector path (fp32 caches, any block size): the same decomposition, one
+// token at a time, lanes owning head dimensions, fp32 FMAs and wave
+// reductions.
+
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct Params {
+  void* out;
+  const void* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t* counters;
+  float2* ws_ml;
+  float* ws_acc;
+  int h_q, h_kv, group, block_size, num_blocks, max_blocks_per_seq;
+  int num_splits, tiles_per_split, units;
+  float scale_log2, v_scale;
+  int out_dtype;
+};
+
+struct Item {
+  int s, kvh, unit, split, ctx, n_tiles, n_splits_seq, t_begin, t_end;
+};
+
+// Workgroup id -> work item.  Consecutive workgroup ids go to the 8 XCDs in
+// turn, so every split of one (sequence, KV head) gets an id with the same
+// residue mod 8: their partial results meet in one XCD's L2.
+__device__ __forceinline__ bool get_item(const Params& p, Item& it) {
+  const int wg = blockIdx.x;
+  const int j = wg >> 3;
+  it.unit = (j / p.num_splits) * 8 + (wg & 7);
+  it.split = j % p.num_splits;
+  if (it.unit >= p.units) return false;
+  it.s = it.unit / p.h_kv;
+  it.kvh = it.unit - it.s * p.h_kv;
+  int ctx = p.context_lens[it.s];
+  const int cap = p.max_blocks_per_seq * p.block_size;
+  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+  it.ctx = ctx;
+  it.n_tiles = (ctx + kTileTokens - 1) / kTileTokens;
+  int ns = (it.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  it.n_splits_seq = ns > p.num_splits ? p.num_splits : ns;
+  const int per = it.n_splits_seq > 0 ? (it.n_tiles + it.n_splits_seq - 1) / it.n_splits_seq : 0;
+  it.t_begin = it.split * per;
+  it.t_end = min(it.n_tiles, it.t_begin + per);
+  return true;
+}
+
+template <int D>
+struct MergeSmem {
+  float acc[kDecodeWaves][kMaxGroup][D + 4];  // +4 floats: rows start on different banks
+  float m[kDecodeWaves][kMaxGroup];
+  float l[kDecodeWaves][kMaxGroup];
+  int flag;
+};
+
+// Store DW = D/16 consecutive outputs (times `mul`) of one output row.
+template <int D>
+__device__ __forceinline__ void store_out(const Params& p, size_t row, int chunk, const float* a, float mul) {
+  constexpr int DW = D / 16;
+  const size_t off = row * D + (size_t)chunk * DW;
+  if (p.out_dtype == kF32) {
+    float* o = static_cast<float*>(p.out) + off;
+#pragma unroll
+    for (int e = 0; e < DW; e += 4) {
+      float4 v = make_float4(a[e] * mul, a[e + 1] * mul, a[e + 2] * mul, a[e + 3] * mul);
+      *reinterpret_cast<float4*>(o + e) = v;
+    }
+  } else {
+    uint16_t* o = static_cast<uint16_t*>(p.out) + off;
+    uint32_t packed[DW / 2];
+#pragma unroll
+    for (int e = 0; e < DW; e += 2) {
+      uint32_t lo, hi;
+      if (p.out_dtype == kBF16) {
+        lo = f32_to_bf16_rne(a[e] * mul);
+        hi = f32_to_bf16_rne(a[e + 1] * mul);
+      } else {
+        lo = f32_to_f16_bits(a[e] * mul);
+        hi = f32_to_f16_bits(a[e + 1] * mul);
+      }
+      packed[e / 2] = lo | (hi << 16);
+    }
+    if constexpr (DW == 8) {
+      *reinterpret_cast<u32x4*>(o) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    } else {
+      *reinterpret_cast<u32x2*>(o) = u32x2{packed[0], packed[1]};
+    }
+  }
+}
+
+// Sequences with an empty context attend over nothing: their output is 0.
+template <int D>
+__device__ void write_zeros(const Params& p, const Item& it) {
+  constexpr int DW = D / 16;
+  const int g = threadIdx.x >> 4, chunk = threadIdx.x & 15;
+  if (g >= p.group) return;
+  float z[DW];
+#pragma unroll
+  for (int e = 0; e < DW; ++e) z[e] = 0.f;
+  store_out<D>(p, (size_t)it.s * p.h_q + it.kvh * p.group + g, chunk, z, 1.f);
+}
+
+// Merge the 4 waves' states (already in `sm`, after a barrier), then either
+// write the output (one range) or publish this range's partial state and let
+// the last range of the (sequence, KV head) combine all of them.
+template <int D>
+__device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
+  constexpr int DW = D / 16;
+  const int t = threadIdx.x;
+  const int g = t >> 4, chunk = t & 15;
+  const int G = p.group;
+  float a[DW];
+  float mstar = kNegInf, lstar = 0.f;
+#pragma unroll
+  for (int e = 0; e < DW; ++e) a[e] = 0.f;
+  if (g < G) {
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) mstar = fmaxf(mstar, sm.m[w][g]);
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float f = mstar == kNegInf ? 0.f : fast_exp2(sm.m[w][g] - mstar);
+      lstar += f * sm.l[w][g];
+#pragma unroll
+      for (int e = 0; e < DW; ++e) a[e] += f * sm.acc[w][g][chunk * DW + e];
+    }
+  }
+  const size_t row = (size_t)it.s * p.h_q + it.kvh * G + g;
+  if (it.n_splits_seq == 1) {
+    if (g < G) store_out<D>(p, row, chunk, a, p.v_scale / lstar);
+    return;
+  }
+  const size_t base = (size_t)it.unit * p.num_splits * G + g;  // partial row of split 0
+  if (g < G) {
+    const size_t prow = base + (size_t)it.split * G;
+    float* dst = p.ws_acc + prow * D + chunk * DW;
+#pragma unroll
+    for (int e = 0; e < DW; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(a[e], a[e + 1], a[e + 2], a[e + 3]);
+    if (chunk == 0) p.ws_ml[prow] = make_float2(mstar, lstar);
+  }
+  __threadfence();  // release this range's partial state device-wide
+  __syncthreads();
+  if (t == 0) {
+    const int prev = atomicAdd(p.counters + it.unit, 1);
+    const int last = prev == it.n_splits_seq - 1;
+    if (last) atomicExch(p.counters + it.unit, 0);  // ready for the next call
+    sm.flag = last;
+  }
+  __syncthreads();
+  if (!sm.flag) return;
+  __threadfence();  // acquire the other ranges' partial states
+  if (g >= G) return;
+  float mm = kNegInf;
+  for (int sp = 0; sp < it.n_splits_seq; ++sp) mm = fmaxf(mm, p.ws_ml[base + (size_t)sp * G].x);
+  float ll = 0.f;
+  float o[DW];
+#pragma unroll
+  for (int e = 0; e < DW; ++e) o[e] = 0.f;
+  for (int sp = 0; sp < it.n_splits_seq; ++sp) {
+    const size_t prow = base + (size_t)sp * G;
+    const float2 ml = p.ws_ml[prow];
+    const float f = mm == kNegInf ? 0.f : fast_exp2(ml.x - mm);
+    ll += f * ml.y;
+    const float* src = p.ws_acc + prow * D + chunk * DW;
+#pragma unroll
+    for (int e = 0; e < DW; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + e);
+      o[e] += f * v.x;
+      o[e + 1] += f * v.y;
+      o[e + 2] += f * v.z;
+      o[e + 3] += f * v.w;
+    }
+  }
+  store_out<D>(p, row, chunk, o, p.v_scale / ll);
+}
+
+// ---------------------------------------------------------------- matrix-core path
+
+template <int CT>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (CT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+}
+
+// Two floats holding values exactly representable in CT -> packed CT pair.
+template <int CT>
+__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+  if constexpr (CT == kBF16) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+}
+
+// Four E4M3 bytes -> four floats (exact).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = a[0];
+  f[1] = a[1];
+  f[2] = b[0];
+  f[3] = b[1];
+}
+
+template <int KV, int D>
+struct MfmaTile {
+  static constexpr int ES = KV == kFP8 ? 1 : 2;  // bytes per cached element
+  static constexpr int ROW = D * ES;              // bytes of one token's row (one head)
+  static constexpr int KCH = ROW / 64;            // 16-byte K chunks per lane
+  static constexpr int VB = D * ES / 16;          // V bytes per lane per token row
+  static constexpr int VDW = VB / 4;              // ... in dwords (1, 2 or 4)
+  u32x4 k[KCH];
+  uint32_t v[4][VDW];
+  int lim;  // valid tokens in the tile (0..16)
+};
+
+template <int KV, int CT, int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(Params p) {
+  using Tile = MfmaTile<KV, D>;
+  constexpr int ROW = Tile::ROW;
+  constexpr int KCH = Tile::KCH;
+  constexpr int VDW = Tile::VDW;
+  constexpr int NK = D / 32;  // MFMA k-steps for the scores
+  constexpr int NT = D / 16;  // 16-row output tiles of the PV product
+  constexpr int DW = D / 16;  // d values per lane in the V transpose
+
+  __shared__ union {
+    u32x2 vt[kDecodeWaves][D][4];  // per-wave V^T tile: [d (swizzled)][token quad] of 4 x 16-bit
+    MergeSmem<D> merge;
+  } sm;
+
+  Item it;
+  if (!get_item(p, it)) return;
+  if (it.n_tiles == 0) {
+    if (it.split == 0) write_zeros<D>(p, it);
+    return;
+  }
+  if (it.split >= it.n_splits_seq) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lo16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int G = p.group;
+
+  // Q as the B operand: column g = lo16, same d order as the K chunks.
+  u32x4 qop[NK];
+  {
+    const int g_load = lo16 < G ? lo16 : G - 1;  // padding rows never form an address past the group
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)it.s * p.h_q + it.kvh * G + g_load) * D;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const int d0 = KV == kFP8 ? 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1) : 32 * kk + 8 * q4;
+      qop[kk] = lo16 < G ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+
+  const int first = it.t_begin + wave;
+  const int n_my = first < it.t_end ? (it.t_end - first + kDecodeWaves - 1) / kDecodeWaves : 0;
+  const int32_t* bt_row = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
+  const size_t head_bytes = (size_t)p.block_size * ROW;
+  const size_t block_bytes = head_bytes * p.h_kv;
+  const uint8_t* kbase = p.k_cache + it.kvh * head_bytes;
+  const uint8_t* vbase = p.v_cache + it.kvh * head_bytes;
+
+  // Block ids of this wave's tiles, 64 at a time, one per lane.
+  int ids = 0, ids_base = -64;
+  auto load_tile = [&](int i, Tile& r) {
+    if (i - ids_base >= 64) {
+      ids_base = i;
+      const int ti = first + kDecodeWaves * (i + lane);
+      ids = ti < it.t_end ? bt_row[(ti * kTileTokens) / p.block_size] : 0;
+    }
+    const int ti = first + kDecodeWaves * i;
+    const int tok0 = ti * kTileTokens;
+    int phys = __builtin_amdgcn_readlane(ids, i - ids_base);
+    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    phys = ok ? phys : 0;
+    const int rem = it.ctx - tok0;
+    r.lim = ok ? (rem < kTileTokens ? rem : kTileTokens) : 0;
+    const size_t off = (size_t)phys * block_bytes + (size_t)(tok0 % p.block_size) * ROW;
+    const uint8_t* kp = kbase + off + lo16 * ROW + q4 * 16;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kp + c * 64);
+    const uint8_t* vp = vbase + off + (4 * q4) * ROW + lo16 * Tile::VB;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      if constexpr (VDW == 4) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(vp + rr * ROW);
+        r.v[rr][0] = x[0];
+        r.v[rr][1] = x[1];
+        r.v[rr][2] = x[2];
+        r.v[rr][3] = x[3];
+      } else if constexpr (VDW == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(vp + rr * ROW);
+        r.v[rr][0] = x[0];
+        r.v[rr][1] = x[1];
+      } else {
+        r.v[rr][0] = *reinterpret_cast<const uint32_t*>(vp + rr * ROW);
+      }
+    }
+  };
+
+  auto compute_tile = [&](Tile& r) {
+    // 1) scores for the 16 tokens of the tile against the (padded) query group
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      u32x4 a;
+      if constexpr (KV == kFP8) {
+        float f[8];
+        fp8x4_to_f32(r.k[kk >> 1][2 * (kk & 1)], f);
+        fp8x4_to_f32(r.k[kk >> 1][2 * (kk & 1) + 1], f + 4);
+        a = u32x4{pack_exact<CT>(f[0], f[1]), pack_exact<CT>(f[2], f[3]), pack_exact<CT>(f[4], f[5]),
+                  pack_exact<CT>(f[6], f[7])};
+      } else {
+        a = r.k[kk];
+      }
+      sc = mfma_16x16x32<CT>(a, qop[kk], sc);
+    }
+
+    // 2) V -> LDS as V^T[d][token quad]; masked rows are zeroed first
+    const bool partial = r.lim < kTileTokens;
+    if (partial) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (4 * q4 + rr >= r.lim) {
+#pragma unroll
+          for (int w = 0; w < VDW; ++w) r.v[rr][w] = 0u;
+        }
+    }
+    if constexpr (KV == kFP8) {
+      float f[4][DW];  // element e of row rr is byte e%4 of dword e/4
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int w = 0; w < VDW; ++w) fp8x4_to_f32(r.v[rr][w], &f[rr][4 * w]);
+#pragma unroll
+      for (int e = 0; e < DW; ++e) {
+        const int d = lo16 * DW + e;
+        sm.vt[wave][d ^ ((d >> 3) & 7)][q4] =
+            u32x2{pack_exact<CT>(f[0][e], f[1][e]), pack_exact<CT>(f[2][e], f[3][e])};
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DW; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+        const int d = lo16 * DW + e;
+        sm.vt[wave][d ^ ((d >> 3) & 7)][q4] = u32x2{__builtin_amdgcn_perm(r.v[1][e >> 1], r.v[0][e >> 1], sel),
+                                                     __builtin_amdgcn_perm(r.v[3][e >> 1], r.v[2][e >> 1], sel)};
+      }
+    }
+    compiler_fence();
+
+    // 3) online softmax (log2 domain); row g = lo16, tokens 4*q4 + rr
+    float s[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      s[rr] = sc[rr] * p.scale_log2;
+      if (partial && 4 * q4 + rr >= r.lim) s[rr] = kNegInf;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float pr[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) pr[rr] = fast_exp2(s[rr] - m_use);
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+
+    // probabilities as hi + lo 16-bit parts (K slots 0-3: hi, 4-7: lo)
+    u32x4 pb;
+    if constexpr (CT == kBF16) {
+      float lo_part[4];
+      uint32_t hb[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        hb[rr] = __float_as_uint(pr[rr]) & 0xffff0000u;
+        lo_part[rr] = pr[rr] - __uint_as_float(hb[rr]);
+      }
+      pb = u32x4{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u), __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u),
+                 __builtin_amdgcn_perm(__float_as_uint(lo_part[1]), __float_as_uint(lo_part[0]), 0x07060302u),
+                 __builtin_amdgcn_perm(__float_as_uint(lo_part[3]), __float_as_uint(lo_part[2]), 0x07060302u)};
+    } else {
+      const auto h01 = __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]);
+      const auto h23 = __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]);
+      const auto l01 = __builtin_amdgcn_cvt_pkrtz(pr[0] - (float)h01[0], pr[1] - (float)h01[1]);
+      const auto l23 = __builtin_amdgcn_cvt_pkrtz(pr[2] - (float)h23[0], pr[3] - (float)h23[1]);
+      pb = u32x4{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23), __builtin_bit_cast(uint32_t, l01),
+                 __builtin_bit_cast(uint32_t, l23)};
+    }
+
+    // 4) O^T += V^T P^T, one MFMA per 16 rows of d
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int d = 16 * n + lo16;
+      const u32x2 cell = sm.vt[wave][d ^ ((d >> 3) & 7)][q4];
+      acc[n] = mfma_16x16x32<CT>(u32x4{cell[0], cell[1], cell[0], cell[1]}, pb, acc[n]);
+    }
+    compiler_fence();
+  };
+
+  // Software pipeline: the next tile's loads are in flight while this one computes.
+  Tile ta, tb;
+  if (n_my > 0) load_tile(0, ta);
+  for (int i = 0; i < n_my; i += 2) {
+    if (i + 1 < n_my) load_tile(i + 1, tb);
+    compute_tile(ta);
+    if (i + 1 >= n_my) break;
+    if (i + 2 < n_my) load_tile(i + 2, ta);
+    compute_tile(tb);
+  }
+
+  float l_row = l_run + shfl_xor_f32(l_run, 16);
+  l_row += shfl_xor_f32(l_row, 32);
+
+  __syncthreads();  // every wave is done with its V^T tile: reuse LDS for the merge
+#pragma unroll
+  for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(&sm.merge.acc[wave][lo16][16 * n + 4 * q4]) = acc[n];
+  if (q4 == 0) {
+    sm.merge.m[wave][lo16] = m_run;
+    sm.merge.l[wave][lo16] = l_row;
+  }
+  __syncthreads();
+  finish<D>(p, it, sm.merge);
+}
+
+// ---------------------------------------------------------------- vector path
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* base, size_t i) {
+  if constexpr (DT == kF32) return static_cast<const float*>(base)[i];
+  else if constexpr (DT == kFP8) return elem_to_f32<kFP8>(static_cast<const uint8_t*>(base)[i]);
+  else return elem_to_f32<DT>(static_cast<const uint16_t*>(base)[i]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f32(v, m);
+  return v;
+}
+
+template <int KV, int QT, int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_vector_kernel(Params p) {
+  constexpr int J = D / 64;
+  __shared__ MergeSmem<D> sm;
+
+  Item it;
+  if (!get_item(p, it)) return;
+  if (it.n_tiles == 0) {
+    if (it.split == 0) write_zeros<D>(p, it);
+    return;
+  }
+  if (it.split >= it.n_splits_seq) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int G = p.group;
+
+  float qv[kMaxGroup][J], acc[kMaxGroup][J], m[kMaxGroup], l[kMaxGroup];
+  const size_t qrow0 = ((size_t)it.s * p.h_q + it.kvh * G) * D;
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float x = load_elem<QT>(p.q, qrow0 + (size_t)(g < G ? g : G - 1) * D + lane + 64 * j);
+      qv[g][j] = g < G ? x : 0.f;
+      acc[g][j] = 0.f;
+    }
+    m[g] = kNegInf;
+    l[g] = 0.f;
+  }
+
+  const int32_t* bt_row = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
+  for (int ti = it.t_begin + wave; ti < it.t_end; ti += kDecodeWaves) {
+    const int t0 = ti * kTileTokens;
+    const int t1 = min(t0 + kTileTokens, it.ctx);
+    for (int t = t0; t < t1; ++t) {
+      const int phys = bt_row[t / p.block_size];
+      if ((unsigned)phys >= (unsigned)p.num_blocks) continue;
+      const size_t row = (((size_t)phys * p.h_kv + it.kvh) * p.block_size + t % p.block_size) * D;
+      float kd[J], vd[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        kd[j] = load_elem<KV>(p.k_cache, row + lane + 64 * j);
+        vd[j] = load_elem<KV>(p.v_cache, row + lane + 64 * j);
+      }
+#pragma unroll
+      for (int g = 0; g < kMaxGroup; ++g) {
+        if (g < G) {
+          float part = 0.f;
+#pragma unroll
+          for (int j = 0; j < J; ++j) part += qv[g][j] * kd[j];
+          const float s = wave_sum(part) * p.scale_log2;
+          const float m_new = fmaxf(m[g], s);
+          const float alpha = fast_exp2(m[g] - m_new);
+          const float pe = fast_exp2(s - m_new);
+          l[g] = l[g] * alpha + pe;
+#pragma unroll
+          for (int j = 0; j < J; ++j) acc[g][j] = acc[g][j] * alpha + pe * vd[j];
+          m[g] = m_new;
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) sm.acc[wave][g][lane + 64 * j] = acc[g][j];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+      sm.m[wave][g] = m[g];
+      sm.l[wave][g] = l[g];
+    }
+  }
+  __syncthreads();
+  finish<D>(p, it, sm);
+}
+
+template <typename K>
+hipError_t launch(K kernel, int grid, const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kDecodeThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
+  if (a.matrix_core) {
+    if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kBF16, kBF16, D>, grid, p, s);
+    if (a.kv_dtype == kF16 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kF16, kF16, D>, grid, p, s);
+    if (a.kv_dtype == kFP8 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kFP8, kBF16, D>, grid, p, s);
+    if (a.kv_dtype == kFP8 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kFP8, kF16, D>, grid, p, s);
+  } else {
+    if (a.kv_dtype == kF32 && a.q_dtype == kF32) return launch(decode_vector_kernel<kF32, kF32, D>, grid, p, s);
+    if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_vector_kernel<kBF16, kBF16, D>, grid, p, s);
+    if (a.kv_dtype == kF16 && a.q_dtype == kF16) return launch(decode_vector_kernel<kF16, kF16, D>, grid, p, s);
+    if (a.kv_dtype == kFP8 && a.q_dtype == kBF16) return launch(decode_vector_kernel<kFP8, kBF16, D>, grid, p, s);
+    if (a.kv_dtype == kFP8 && a.q_dtype == kF16) return launch(decode_vector_kernel<kFP8, kF16, D>, grid, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits) {
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t units = (size_t)num_seqs * h_kv;
+  const size_t rows = (size_t)num_seqs * h_q * num_splits;  // units * G * splits
+  WorkspaceLayout L;
+  L.counters = 0;
+  L.ml = align(units * sizeof(int32_t));
+  L.acc = L.ml + align(rows * sizeof(float2));
+  L.total = L.acc + align(rows * head_dim * sizeof(float));
+  return L;
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
+  const WorkspaceLayout L = decode_workspace_layout(a.num_seqs, a.h_q, a.h_kv, a.head_dim, a.num_splits);
+  Params p;
+  p.out = a.out;
+  p.q = a.q;
+  p.k_cache = static_cast<const uint8_t*>(a.k_cache);
+  p.v_cache = static_cast<const uint8_t*>(a.v_cache);
+  p.block_tables = a.block_tables;
+  p.context_lens = a.context_lens;
+  char* ws = static_cast<char*>(a.workspace);
+  p.counters = reinterpret_cast<int32_t*>(ws + L.counters);
+  p.ws_ml = reinterpret_cast<float2*>(ws + L.ml);
+  p.ws_acc = reinterpret_cast<float*>(ws + L.acc);
+  p.h_q = a.h_q;
+  p.h_kv = a.h_kv;
+  p.group = a.h_q / a.h_kv;
+  p.block_size = a.block_size;
+  p.num_blocks = a.num_blocks;
+  p.max_blocks_per_seq = a.max_blocks_per_seq;
+  p.num_splits = a.num_splits;
+  p.tiles_per_split = a.tiles_per_split;
+  p.units = a.num_seqs * a.h_kv;
+  p.scale_log2 = a.scale_log2;
+  p.v_scale = a.v_scale;
+  p.out_dtype = a.out_dtype;
+  const int grid = ((p.units + 7) / 8) * 8 * a.num_splits;
+  if (grid == 0) return hipSuccess;
+  if (a.head_dim == 128) return dispatch<128>(a, grid, p, stream);
+  if (a.head_dim == 64) return dispatch<64>(a, grid, p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -1,0 +1,51 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kDecodeWaves = 4;        // waves per decode workgroup
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kTileTokens = 16;        // tokens per matrix-core tile
+constexpr int kMaxGroup = 16;          // query heads per KV head handled by one workgroup
+
+struct DecodeLaunch {
+  void* out;
+  int out_dtype;
+  const void* q;
+  int q_dtype;
+  const void* k_cache;
+  const void* v_cache;
+  int kv_dtype;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs, h_q, h_kv, head_dim, block_size, num_blocks, max_blocks_per_seq;
+  int num_splits;       // workgroups per (sequence, KV head)
+  int tiles_per_split;  // upper bound of 16-token tiles per workgroup
+  float scale_log2;     // logit scale * log2(e), times k_scale for FP8 caches
+  float v_scale;        // output scale (FP8 V), else 1
+  void* workspace;
+  bool matrix_core;     // MFMA path (else the vector path)
+};
+
+// Byte layout of the decode workspace.
+struct WorkspaceLayout {
+  size_t counters;  // int32 [units]
+  size_t ml;        // float2 [units, splits, G]  (running max, running sum)
+  size_t acc;       // float [units, splits, G, D]
+  size_t total;
+};
+
+WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits);
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, int in_dtype, void* k_cache, void* v_cache,
+                                    int kv_dtype, float k_scale, float v_scale, const int64_t* slot_mapping,
+                                    int num_tokens, int h_kv, int head_dim, int block_size, int num_blocks,
+                                    hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,153 @@
+// reshape_and_cache: write each new token's K and V into its slot of the
+// paged pool, for gfx950.
+//
+// A sequence grows by claiming free blocks without relocating earlier ones
+// ("Paged KV Cache" tutorial, section "Answer Key", question 2), so the new
+// token of a decode step writes exactly one slot: slot = block * B + offset,
+// landing at cache[slot / B, head, slot % B, :].
+//
+// One thread moves 8 consecutive elements of one (token, head): 16-byte
+// loads/stores for 16-bit data.  Into an FP8 pool each element is divided by
+// the tensor scale (one correctly rounded binary32 division) and rounded to
+// the nearest E4M3 code with saturation.
+
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct Chunk8;  // 8 elements of storage type DT
+template <>
+struct Chunk8<kF32> {
+  u32x4 w[2];
+};
+template <>
+struct Chunk8<kF16> {
+  u32x4 w;
+};
+template <>
+struct Chunk8<kBF16> {
+  u32x4 w;
+};
+template <>
+struct Chunk8<kFP8> {
+  u32x2 w;
+};
+
+template <int DT>
+__device__ __forceinline__ Chunk8<DT> load8(const uint8_t* p) {
+  Chunk8<DT> c;
+  if constexpr (DT == kF32) {
+    c.w[0] = reinterpret_cast<const u32x4*>(p)[0];
+    c.w[1] = reinterpret_cast<const u32x4*>(p)[1];
+  } else if constexpr (DT == kFP8) {
+    c.w = *reinterpret_cast<const u32x2*>(p);
+  } else {
+    c.w = *reinterpret_cast<const u32x4*>(p);
+  }
+  return c;
+}
+
+template <int DT>
+__device__ __forceinline__ void store8(uint8_t* p, const Chunk8<DT>& c) {
+  if constexpr (DT == kF32) {
+    reinterpret_cast<u32x4*>(p)[0] = c.w[0];
+    reinterpret_cast<u32x4*>(p)[1] = c.w[1];
+  } else if constexpr (DT == kFP8) {
+    *reinterpret_cast<u32x2*>(p) = c.w;
+  } else {
+    *reinterpret_cast<u32x4*>(p) = c.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float chunk_elem(const Chunk8<DT>& c, int e) {
+  if constexpr (DT == kF32) {
+    return __uint_as_float(c.w[e >> 2][e & 3]);
+  } else {
+    const uint32_t word = c.w[e >> 1];
+    return elem_to_f32<DT>((e & 1) ? (word >> 16) : (word & 0xffffu));
+  }
+}
+
+template <int IN>
+__device__ __forceinline__ Chunk8<kFP8> quantize8(const Chunk8<IN>& c, float scale) {
+  uint32_t b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = f32_to_e4m3_sat(__fdiv_rn(chunk_elem<IN>(c, e), scale));
+  Chunk8<kFP8> o;
+  o.w = u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+  return o;
+}
+
+constexpr int kEsize[4] = {4, 2, 2, 1};
+
+template <int IN, int KV>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(const uint8_t* key, const uint8_t* value,
+                                                                uint8_t* k_cache, uint8_t* v_cache,
+                                                                const int64_t* slots, int num_tokens, int h_kv,
+                                                                int head_dim, int block_size, int num_blocks,
+                                                                float k_scale, float v_scale) {
+  const int chunks = head_dim / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)num_tokens * h_kv * chunks) return;
+  const int c = (int)(gid % chunks);
+  const int64_t th = gid / chunks;
+  const int h = (int)(th % h_kv);
+  const int64_t t = th / h_kv;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;  // padding or outside the pool
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int64_t src = ((t * h_kv + h) * head_dim + (int64_t)c * 8) * kEsize[IN];
+  const int64_t dst = (((blk * h_kv + h) * block_size + off) * head_dim + (int64_t)c * 8) * kEsize[KV];
+  const Chunk8<IN> kin = load8<IN>(key + src);
+  const Chunk8<IN> vin = load8<IN>(value + src);
+  if constexpr (IN == KV) {
+    store8<KV>(k_cache + dst, kin);
+    store8<KV>(v_cache + dst, vin);
+  } else {
+    store8<kFP8>(k_cache + dst, quantize8<IN>(kin, k_scale));
+    store8<kFP8>(v_cache + dst, quantize8<IN>(vin, v_scale));
+  }
+}
+
+template <int IN, int KV>
+hipError_t launch(const void* key, const void* value, void* kc, void* vc, const int64_t* slots, int T, int h_kv,
+                  int d, int bs, int nb, float ks, float vs, hipStream_t stream) {
+  const int64_t threads = (int64_t)T * h_kv * (d / 8);
+  if (threads == 0) return hipSuccess;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((reshape_and_cache_kernel<IN, KV>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value), static_cast<uint8_t*>(kc),
+                     static_cast<uint8_t*>(vc), slots, T, h_kv, d, bs, nb, ks, vs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, int in_dtype, void* k_cache, void* v_cache,
+                                    int kv_dtype, float k_scale, float v_scale, const int64_t* slot_mapping,
+                                    int num_tokens, int h_kv, int head_dim, int block_size, int num_blocks,
+                                    hipStream_t stream) {
+#define PKV_RC(IN, KV)                                                                                          \
+  if (in_dtype == IN && kv_dtype == KV)                                                                         \
+    return launch<IN, KV>(key, value, k_cache, v_cache, slot_mapping, num_tokens, h_kv, head_dim, block_size, \
+                          num_blocks, k_scale, v_scale, stream);
+  PKV_RC(kF32, kF32)
+  PKV_RC(kF16, kF16)
+  PKV_RC(kBF16, kBF16)
+  PKV_RC(kFP8, kFP8)
+  PKV_RC(kF32, kFP8)
+  PKV_RC(kF16, kFP8)
+  PKV_RC(kBF16, kFP8)
+#undef PKV_RC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv
