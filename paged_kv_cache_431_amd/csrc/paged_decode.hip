@@ -11,13 +11,23 @@
 // Work decomposition
 //   One workgroup (4 waves) per (sequence, KV head, split).  The sequence's
 //   16-token tiles are cut into `n` contiguous ranges (n <= num_splits, chosen
-//   per sequence on the device from its own length); within a range, wave w
-//   takes tiles w, w+4, w+8, ...  Each wave keeps an online-softmax state
-//   (running max m, running sum l, unnormalised output acc) per query row; the
-//   4 waves merge through LDS; a sequence with several ranges writes partial
-//   states to the workspace and the last workgroup to finish (an atomic
-//   counter per (sequence, KV head)) merges them and writes the output, so a
-//   call is a single kernel launch.
+//   per sequence on the device from its own length); each wave takes a
+//   contiguous quarter of its workgroup's range.  Each wave keeps an
+//   online-softmax state (running max m, running sum l, unnormalised output
+//   acc) per query row; the 4 waves merge through LDS; a sequence with several
+//   ranges writes partial states to the workspace and the last workgroup to
+//   finish (an atomic counter per (sequence, KV head)) merges them and writes
+//   the output, so a call is a single kernel launch.
+//
+// Memory pipeline (the kernel is bound by HBM bandwidth: each K/V byte is
+// used by G query rows only)
+//   A wave first loads the physical block ids of up to 64 of its tiles, one
+//   per lane, then streams the tiles through a ring of NBUF register buffers:
+//   while tile i is computed, the loads of the next NBUF-1 tiles are in
+//   flight.  Loads are issued unconditionally (a step past the end re-reads
+//   the wave's last tile, which the L2 serves, and computes nothing), so the
+//   compiler can wait for exactly the oldest tile instead of draining every
+//   outstanding load.
 //
 // Matrix-core path (16-bit or FP8 caches, block_size a multiple of 16)
 //   Scores: S^T[token][g] = K[token][:] . Q[g][:] with v_mfma_f32_16x16x32
@@ -42,6 +52,15 @@
 //   Tokens past the context (the tail of the last block) are masked by select,
 //   never by multiplying, so whatever those slots hold (NaN included) cannot
 //   leak into the result.
+//   The running max moves only when a score exceeds it by more than
+//   kRescaleSlack (log2 units), so after the first tiles the accumulators are
+//   rarely rescaled; probabilities relative to the stale max stay <= 2^8.
+//
+// Cross-split merge
+//   Partial states are written and read with device-scope (agent) relaxed
+//   atomic stores and loads, which the gfx950 memory system keeps coherent
+//   across the XCDs' separate L2 caches without writing back or invalidating
+//   whole caches; a vmcnt(0) wait orders them before the counter increment.
 //
 // Vector path (fp32 caches, any block size): the same decomposition, one
 // token at a time, lanes owning head dimensions, fp32 FMAs and wave
@@ -57,6 +76,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleSlack = 8.0f;
 
 struct Params {
   void* out;
@@ -66,8 +86,8 @@ struct Params {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int32_t* counters;
-  float2* ws_ml;
-  float* ws_acc;
+  float* ws_ml;   // [rows][2]: running max, running sum
+  float* ws_acc;  // [rows][D]
   int h_q, h_kv, group, block_size, num_blocks, max_blocks_per_seq;
   int num_splits, tiles_per_split, units;
   float scale_log2, v_scale;
@@ -109,6 +129,17 @@ struct MergeSmem {
   float l[kDecodeWaves][kMaxGroup];
   int flag;
 };
+
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every store this wave issued has completed.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Store DW = D/16 consecutive outputs (times `mul`) of one output row.
 template <int D>
@@ -191,41 +222,38 @@ __device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
     const size_t prow = base + (size_t)it.split * G;
     float* dst = p.ws_acc + prow * D + chunk * DW;
 #pragma unroll
-    for (int e = 0; e < DW; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(a[e], a[e + 1], a[e + 2], a[e + 3]);
-    if (chunk == 0) p.ws_ml[prow] = make_float2(mstar, lstar);
+    for (int e = 0; e < DW; ++e) store_agent(dst + e, a[e]);
+    if (chunk == 0) {
+      store_agent(p.ws_ml + 2 * prow, mstar);
+      store_agent(p.ws_ml + 2 * prow + 1, lstar);
+    }
   }
-  __threadfence();  // release this range's partial state device-wide
+  wait_vm();  // this range's partial state is complete device-wide before it is counted
   __syncthreads();
   if (t == 0) {
-    const int prev = atomicAdd(p.counters + it.unit, 1);
+    const int prev = __hip_atomic_fetch_add(p.counters + it.unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == it.n_splits_seq - 1;
-    if (last) atomicExch(p.counters + it.unit, 0);  // ready for the next call
+    if (last) __hip_atomic_store(p.counters + it.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.flag = last;
   }
   __syncthreads();
   if (!sm.flag) return;
-  __threadfence();  // acquire the other ranges' partial states
   if (g >= G) return;
   float mm = kNegInf;
-  for (int sp = 0; sp < it.n_splits_seq; ++sp) mm = fmaxf(mm, p.ws_ml[base + (size_t)sp * G].x);
+  for (int sp = 0; sp < it.n_splits_seq; ++sp) mm = fmaxf(mm, load_agent(p.ws_ml + 2 * (base + (size_t)sp * G)));
   float ll = 0.f;
   float o[DW];
 #pragma unroll
   for (int e = 0; e < DW; ++e) o[e] = 0.f;
   for (int sp = 0; sp < it.n_splits_seq; ++sp) {
     const size_t prow = base + (size_t)sp * G;
-    const float2 ml = p.ws_ml[prow];
-    const float f = mm == kNegInf ? 0.f : fast_exp2(ml.x - mm);
-    ll += f * ml.y;
+    const float m_i = load_agent(p.ws_ml + 2 * prow);
+    const float l_i = load_agent(p.ws_ml + 2 * prow + 1);
+    const float f = mm == kNegInf ? 0.f : fast_exp2(m_i - mm);
+    ll += f * l_i;
     const float* src = p.ws_acc + prow * D + chunk * DW;
 #pragma unroll
-    for (int e = 0; e < DW; e += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(src + e);
-      o[e] += f * v.x;
-      o[e + 1] += f * v.y;
-      o[e + 2] += f * v.z;
-      o[e + 3] += f * v.w;
-    }
+    for (int e = 0; e < DW; ++e) o[e] += f * load_agent(src + e);
   }
   store_out<D>(p, row, chunk, o, p.v_scale / ll);
 }
@@ -270,17 +298,22 @@ struct MfmaTile {
   static constexpr int KCH = ROW / 64;            // 16-byte K chunks per lane
   static constexpr int VB = D * ES / 16;          // V bytes per lane per token row
   static constexpr int VDW = VB / 4;              // ... in dwords (1, 2 or 4)
+  // Register buffers in the load ring: two when a tile takes 32 VGPRs per
+  // lane (16-bit, D = 128), else three.
+  static constexpr int NBUF = (D == 128 || KCH * 4 + 4 * VDW > 16) ? 2 : 3;
   u32x4 k[KCH];
   uint32_t v[4][VDW];
   int lim;  // valid tokens in the tile (0..16)
 };
 
 template <int KV, int CT, int D>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(Params p) {
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
+    Params p) {
   using Tile = MfmaTile<KV, D>;
   constexpr int ROW = Tile::ROW;
   constexpr int KCH = Tile::KCH;
   constexpr int VDW = Tile::VDW;
+  constexpr int NBUF = Tile::NBUF;
   constexpr int NK = D / 32;  // MFMA k-steps for the scores
   constexpr int NT = D / 16;  // 16-row output tiles of the PV product
   constexpr int DW = D / 16;  // d values per lane in the V transpose
@@ -321,53 +354,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(Params p) {
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  const int first = it.t_begin + wave;
-  const int n_my = first < it.t_end ? (it.t_end - first + kDecodeWaves - 1) / kDecodeWaves : 0;
+  // This wave's tiles: a contiguous slice [wb, wb + n_my) of the range.
+  const int span = it.t_end - it.t_begin;
+  const int per_w = span > 0 ? (span + kDecodeWaves - 1) / kDecodeWaves : 0;
+  const int wb = it.t_begin + wave * per_w;
+  const int n_my = max(0, min(it.t_end, wb + per_w) - wb);
+
   const int32_t* bt_row = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
   const size_t head_bytes = (size_t)p.block_size * ROW;
   const size_t block_bytes = head_bytes * p.h_kv;
-  const uint8_t* kbase = p.k_cache + it.kvh * head_bytes;
-  const uint8_t* vbase = p.v_cache + it.kvh * head_bytes;
+  const uint8_t* kbase = p.k_cache + it.kvh * head_bytes + lo16 * ROW + q4 * 16;
+  const uint8_t* vbase = p.v_cache + it.kvh * head_bytes + (4 * q4) * ROW + lo16 * Tile::VB;
 
-  // Block ids of this wave's tiles, 64 at a time, one per lane.
-  int ids = 0, ids_base = -64;
-  auto load_tile = [&](int i, Tile& r) {
-    if (i - ids_base >= 64) {
-      ids_base = i;
-      const int ti = first + kDecodeWaves * (i + lane);
-      ids = ti < it.t_end ? bt_row[(ti * kTileTokens) / p.block_size] : 0;
-    }
-    const int ti = first + kDecodeWaves * i;
-    const int tok0 = ti * kTileTokens;
-    int phys = __builtin_amdgcn_readlane(ids, i - ids_base);
-    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
-    phys = ok ? phys : 0;
-    const int rem = it.ctx - tok0;
-    r.lim = ok ? (rem < kTileTokens ? rem : kTileTokens) : 0;
-    const size_t off = (size_t)phys * block_bytes + (size_t)(tok0 % p.block_size) * ROW;
-    const uint8_t* kp = kbase + off + lo16 * ROW + q4 * 16;
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kp + c * 64);
-    const uint8_t* vp = vbase + off + (4 * q4) * ROW + lo16 * Tile::VB;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      if constexpr (VDW == 4) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vp + rr * ROW);
-        r.v[rr][0] = x[0];
-        r.v[rr][1] = x[1];
-        r.v[rr][2] = x[2];
-        r.v[rr][3] = x[3];
-      } else if constexpr (VDW == 2) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vp + rr * ROW);
-        r.v[rr][0] = x[0];
-        r.v[rr][1] = x[1];
-      } else {
-        r.v[rr][0] = *reinterpret_cast<const uint32_t*>(vp + rr * ROW);
-      }
-    }
-  };
-
-  auto compute_tile = [&](Tile& r) {
+  auto compute_tile = [&](Tile& r, bool valid) {
+    const int lim = valid ? r.lim : 0;
     // 1) scores for the 16 tokens of the tile against the (padded) query group
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -386,26 +386,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(Params p) {
     }
 
     // 2) V -> LDS as V^T[d][token quad]; masked rows are zeroed first
-    const bool partial = r.lim < kTileTokens;
+    const bool partial = lim < kTileTokens;
     if (partial) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        if (4 * q4 + rr >= r.lim) {
+        if (4 * q4 + rr >= lim) {
 #pragma unroll
           for (int w = 0; w < VDW; ++w) r.v[rr][w] = 0u;
         }
     }
     if constexpr (KV == kFP8) {
-      float f[4][DW];  // element e of row rr is byte e%4 of dword e/4
+      // one dword (4 elements) of each of the 4 rows at a time: element
+      // e = 4 * w + x of row rr is byte x of dword w
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
+      for (int w = 0; w < VDW; ++w) {
+        float f[4][4];
 #pragma unroll
-        for (int w = 0; w < VDW; ++w) fp8x4_to_f32(r.v[rr][w], &f[rr][4 * w]);
+        for (int rr = 0; rr < 4; ++rr) fp8x4_to_f32(r.v[rr][w], f[rr]);
 #pragma unroll
-      for (int e = 0; e < DW; ++e) {
-        const int d = lo16 * DW + e;
-        sm.vt[wave][d ^ ((d >> 3) & 7)][q4] =
-            u32x2{pack_exact<CT>(f[0][e], f[1][e]), pack_exact<CT>(f[2][e], f[3][e])};
+        for (int x = 0; x < 4; ++x) {
+          const int d = lo16 * DW + 4 * w + x;
+          sm.vt[wave][d ^ ((d >> 3) & 7)][q4] =
+              u32x2{pack_exact<CT>(f[0][x], f[1][x]), pack_exact<CT>(f[2][x], f[3][x])};
+        }
       }
     } else {
 #pragma unroll
@@ -423,21 +426,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(Params p) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       s[rr] = sc[rr] * p.scale_log2;
-      if (partial && 4 * q4 + rr >= r.lim) s[rr] = kNegInf;
+      if (partial && 4 * q4 + rr >= lim) s[rr] = kNegInf;
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = fmaxf(mx, shfl_xor_f32(mx, 16));
     mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // Move the running max only when this tile exceeds it by more than the
+    // slack (always true for the first tile with a finite score).
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run is -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float pr[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) pr[rr] = fast_exp2(s[rr] - m_use);
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     // probabilities as hi + lo 16-bit parts (K slots 0-3: hi, 4-7: lo)
     u32x4 pb;
@@ -471,15 +480,54 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(Params p) {
     compiler_fence();
   };
 
-  // Software pipeline: the next tile's loads are in flight while this one computes.
-  Tile ta, tb;
-  if (n_my > 0) load_tile(0, ta);
-  for (int i = 0; i < n_my; i += 2) {
-    if (i + 1 < n_my) load_tile(i + 1, tb);
-    compute_tile(ta);
-    if (i + 1 >= n_my) break;
-    if (i + 2 < n_my) load_tile(i + 2, ta);
-    compute_tile(tb);
+  for (int c0 = 0; c0 < n_my; c0 += 64) {
+    const int cn = min(64, n_my - c0);  // tiles in this chunk (>= 1)
+    const int t0 = wb + c0;             // its first tile
+    // Lane j holds the physical block of tile t0 + j (clamped into the chunk,
+    // so only table entries of blocks the context covers are read).
+    const int ids = bt_row[((t0 + min(lane, cn - 1)) * kTileTokens) / p.block_size];
+
+    auto load_tile = [&](Tile& r, int j) {  // j: tile of the chunk, 0 <= j < cn (wave-uniform)
+      const int tok0 = (t0 + j) * kTileTokens;
+      int phys = __builtin_amdgcn_readlane(ids, j);
+      const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+      phys = ok ? phys : 0;
+      const int rem = it.ctx - tok0;
+      r.lim = ok ? (rem < kTileTokens ? rem : kTileTokens) : 0;
+      const size_t off = (size_t)phys * block_bytes + (size_t)(tok0 % p.block_size) * ROW;
+      const uint8_t* kp = kbase + off;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kp + c * 64);
+      const uint8_t* vp = vbase + off;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        if constexpr (VDW == 4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(vp + rr * ROW);
+          r.v[rr][0] = x[0];
+          r.v[rr][1] = x[1];
+          r.v[rr][2] = x[2];
+          r.v[rr][3] = x[3];
+        } else if constexpr (VDW == 2) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(vp + rr * ROW);
+          r.v[rr][0] = x[0];
+          r.v[rr][1] = x[1];
+        } else {
+          r.v[rr][0] = *reinterpret_cast<const uint32_t*>(vp + rr * ROW);
+        }
+      }
+    };
+
+    // Ring of NBUF buffers: tile i + NBUF - 1 is loaded while tile i is computed.
+    Tile buf[NBUF];
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b) load_tile(buf[b], min(b, cn - 1));
+    for (int i = 0; i < cn; i += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        load_tile(buf[(b + NBUF - 1) % NBUF], min(i + b + NBUF - 1, cn - 1));
+        compute_tile(buf[b], i + b < cn);
+      }
+    }
   }
 
   float l_row = l_run + shfl_xor_f32(l_run, 16);
@@ -623,7 +671,7 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int hea
   WorkspaceLayout L;
   L.counters = 0;
   L.ml = align(units * sizeof(int32_t));
-  L.acc = L.ml + align(rows * sizeof(float2));
+  L.acc = L.ml + align(rows * 2 * sizeof(float));
   L.total = L.acc + align(rows * head_dim * sizeof(float));
   return L;
 }
@@ -639,7 +687,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.context_lens = a.context_lens;
   char* ws = static_cast<char*>(a.workspace);
   p.counters = reinterpret_cast<int32_t*>(ws + L.counters);
-  p.ws_ml = reinterpret_cast<float2*>(ws + L.ml);
+  p.ws_ml = reinterpret_cast<float*>(ws + L.ml);
   p.ws_acc = reinterpret_cast<float*>(ws + L.acc);
   p.h_q = a.h_q;
   p.h_kv = a.h_kv;
