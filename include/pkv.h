@@ -85,6 +85,7 @@ int pkv_abi_version(void);
  *   context_lens [S] int32        ctx_s: tokens attended by seq s; positions
  *                                  t >= ctx_s are never read (their bytes may
  *                                  be anything, NaN included)
+ * A 16-bit out_dtype receives the fp32 result rounded to nearest-even.
  * Semantics: for each seq s and query head g (kv head h = g / (Hq / Hkv)):
  *   out[s, g, :] = sum_t softmax_t(scale * q[s, g, :] . K_s[h, t, :]) V_s[h, t, :]
  * over t in [0, ctx_s), where K_s[h, t, :] = k_cache[block_tables[s, t / B],

@@ -12,19 +12,21 @@
 
 namespace {
 
-// Workgroups of the decode kernel resident at once on an MI355X: 256 compute
-// units, 3 four-wave workgroups each (the matrix-core kernel's register use
-// allows 3 waves per SIMD).  Only used to size the split over blocks.
-constexpr int64_t kResidentWorkgroups = 256 * 3;
+constexpr int64_t kResidentWorkgroups = pkv::kResidentDecodeWorkgroups;
 
 bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Number of workgroups that share one (sequence, KV head): minimise
-// (rounds of resident workgroups) x (per-workgroup time), with the time of a
-// workgroup counted in tiles per wave plus a fixed cost for its prologue and
-// epilogue and one more tile's worth for the cross-split merge.
+// (rounds of resident workgroups) x (time of one workgroup), the time counted
+// in 16-token tiles per wave plus fixed costs measured on MI355X: about two
+// tiles' worth for a workgroup's start (context length, block ids, first
+// tile) and about six for the cross-split merge of partial states.  Ties go
+// to the smaller count.
+constexpr int64_t kStartCost = 2;
+constexpr int64_t kMergeCost = 6;
+
 int choose_splits(int64_t units, int64_t max_tiles) {
   if (max_tiles <= 1 || units <= 0) return 1;
   const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(max_tiles, 8)));
@@ -34,7 +36,7 @@ int choose_splits(int64_t units, int64_t max_tiles) {
   for (int64_t n = 1; n <= cap; ++n) {
     const int64_t rounds = ceil_div(padded_units * n, kResidentWorkgroups);
     const int64_t per_wave = ceil_div(ceil_div(max_tiles, n), pkv::kDecodeWaves);
-    const int64_t cost = rounds * (per_wave + 2 + (n > 1 ? 1 : 0));
+    const int64_t cost = rounds * (per_wave + kStartCost + (n > 1 ? kMergeCost : 0));
     if (cost < best_cost) {
       best_cost = cost;
       best = (int)n;
@@ -138,7 +140,11 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, int q_dt
   a.scale_log2 = (float)(s * log2e * (fp8 ? (double)k_scale : 1.0));
   a.v_scale = fp8 ? v_scale : 1.f;
   a.workspace = workspace;
-  a.matrix_core = kv_dtype != PKV_F32 && block_size % pkv::kTileTokens == 0;
+  // matrix-core path: 16-bit or FP8 caches whose blocks hold a power-of-two
+  // number of 16-token tiles; everything else takes the vector path
+  const int tiles_per_block = block_size / pkv::kTileTokens;
+  a.matrix_core = kv_dtype != PKV_F32 && block_size % pkv::kTileTokens == 0 &&
+                  (tiles_per_block & (tiles_per_block - 1)) == 0;
   const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

@@ -90,6 +90,7 @@ struct Params {
   float* ws_acc;  // [rows][D]
   int h_q, h_kv, group, block_size, num_blocks, max_blocks_per_seq;
   int num_splits, tiles_per_split, units;
+  int tile_shift;  // log2(block_size / 16) on the matrix-core path
   float scale_log2, v_scale;
   int out_dtype;
 };
@@ -158,13 +159,18 @@ __device__ __forceinline__ void store_out(const Params& p, size_t row, int chunk
     uint32_t packed[DW / 2];
 #pragma unroll
     for (int e = 0; e < DW; e += 2) {
+      // A 16-bit output is the fp32 output rounded to nearest-even: the
+      // products stay rounded fp32 values (the compiler would otherwise fuse
+      // the multiply into a mixed-precision instruction that rounds once).
+      float y0 = a[e] * mul, y1 = a[e + 1] * mul;
+      asm volatile("" : "+v"(y0), "+v"(y1));
       uint32_t lo, hi;
       if (p.out_dtype == kBF16) {
-        lo = f32_to_bf16_rne(a[e] * mul);
-        hi = f32_to_bf16_rne(a[e + 1] * mul);
+        lo = f32_to_bf16_rne(y0);
+        hi = f32_to_bf16_rne(y1);
       } else {
-        lo = f32_to_f16_bits(a[e] * mul);
-        hi = f32_to_f16_bits(a[e + 1] * mul);
+        lo = f32_to_f16_bits(y0);
+        hi = f32_to_f16_bits(y1);
       }
       packed[e / 2] = lo | (hi << 16);
     }
@@ -271,6 +277,29 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
+template <int CT>
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  if constexpr (CT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b),
+                                                     c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
+                                                 0, 0);
+  }
+}
+
+// Issue spacing after a group of MFMAs.  With the toolchain in use, vector
+// instructions that overwrote a source register of a v_mfma_f32_16x16x32 (its
+// A operand or its accumulator input; 8 passes on gfx950) a few instructions
+// after issue gave wrong results.  Each group is therefore issued with no
+// other instruction in between (the scheduler is kept out) and followed by 16
+// wait states, which cover every read of the operands of its last MFMA.
+__device__ __forceinline__ void mfma_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Two floats holding values exactly representable in CT -> packed CT pair.
 template <int CT>
 __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
@@ -298,16 +327,19 @@ struct MfmaTile {
   static constexpr int KCH = ROW / 64;            // 16-byte K chunks per lane
   static constexpr int VB = D * ES / 16;          // V bytes per lane per token row
   static constexpr int VDW = VB / 4;              // ... in dwords (1, 2 or 4)
-  // Register buffers in the load ring: two when a tile takes 32 VGPRs per
-  // lane (16-bit, D = 128), else three.
-  static constexpr int NBUF = (D == 128 || KCH * 4 + 4 * VDW > 16) ? 2 : 3;
+  // Bytes of K and V one 16-token tile brings in.
+  static constexpr int TILE_BYTES = 2 * kTileTokens * ROW;
+  // Register buffers in the load ring (tile i + NBUF - 1 is loaded while
+  // tile i is computed): two for 8 KiB tiles, three for smaller ones, which
+  // keeps the kernel within the register budget of 3 waves per SIMD.
+  static constexpr int NBUF = TILE_BYTES >= 8192 ? 2 : 3;
   u32x4 k[KCH];
   uint32_t v[4][VDW];
   int lim;  // valid tokens in the tile (0..16)
 };
 
 template <int KV, int CT, int D>
-__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd))) void decode_mfma_kernel(
     Params p) {
   using Tile = MfmaTile<KV, D>;
   constexpr int ROW = Tile::ROW;
@@ -332,7 +364,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   if (it.split >= it.n_splits_seq) return;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform (the compiler cannot tell on its own), so every per-wave
+  // quantity below lives in scalar registers and the tile loop is uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lo16 = lane & 15;
   const int q4 = lane >> 4;
   const int G = p.group;
@@ -384,6 +418,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       }
       sc = mfma_16x16x32<CT>(a, qop[kk], sc);
     }
+    mfma_guard();
 
     // 2) V -> LDS as V^T[d][token quad]; masked rows are zeroed first
     const bool partial = lim < kTileTokens;
@@ -428,13 +463,16 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       s[rr] = sc[rr] * p.scale_log2;
       if (partial && 4 * q4 + rr >= lim) s[rr] = kNegInf;
     }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-    // Move the running max only when this tile exceeds it by more than the
-    // slack (always true for the first tile with a finite score).
-    const bool grow = mx > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    // Each lane tests its own 4 scores against its row's running max.  Only
+    // when a lane of the wave exceeds it by more than the slack (always for
+    // the first tile with a finite score) are the row maxima formed across
+    // the 4 lanes of each row and the state rescaled; otherwise the tile
+    // needs no cross-lane step at all.
+    const float mx_lane = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__builtin_amdgcn_ballot_w64(mx_lane > m_run + kRescaleSlack) != 0) {
+      float mx = fmaxf(mx_lane, shfl_xor_f32(mx_lane, 16));
+      mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+      const bool grow = mx > m_run + kRescaleSlack;  // the same on the 4 lanes of a row
       const float m_new = grow ? mx : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run is -inf
       l_run *= alpha;
@@ -448,8 +486,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     for (int rr = 0; rr < 4; ++rr) pr[rr] = fast_exp2(s[rr] - m_use);
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
-    // probabilities as hi + lo 16-bit parts (K slots 0-3: hi, 4-7: lo)
-    u32x4 pb;
+    // probabilities of tokens 4*q4 .. 4*q4+3 as hi + lo 16-bit parts
+    // (p = hi + lo + O(2^-16 p)), the B operands of the PV products
+    u32x2 p_hi, p_lo;
     if constexpr (CT == kBF16) {
       float lo_part[4];
       uint32_t hb[4];
@@ -458,25 +497,32 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         hb[rr] = __float_as_uint(pr[rr]) & 0xffff0000u;
         lo_part[rr] = pr[rr] - __uint_as_float(hb[rr]);
       }
-      pb = u32x4{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u), __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u),
-                 __builtin_amdgcn_perm(__float_as_uint(lo_part[1]), __float_as_uint(lo_part[0]), 0x07060302u),
-                 __builtin_amdgcn_perm(__float_as_uint(lo_part[3]), __float_as_uint(lo_part[2]), 0x07060302u)};
+      p_hi = u32x2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u), __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
+      p_lo = u32x2{__builtin_amdgcn_perm(__float_as_uint(lo_part[1]), __float_as_uint(lo_part[0]), 0x07060302u),
+                   __builtin_amdgcn_perm(__float_as_uint(lo_part[3]), __float_as_uint(lo_part[2]), 0x07060302u)};
     } else {
       const auto h01 = __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]);
       const auto h23 = __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]);
       const auto l01 = __builtin_amdgcn_cvt_pkrtz(pr[0] - (float)h01[0], pr[1] - (float)h01[1]);
       const auto l23 = __builtin_amdgcn_cvt_pkrtz(pr[2] - (float)h23[0], pr[3] - (float)h23[1]);
-      pb = u32x4{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23), __builtin_bit_cast(uint32_t, l01),
-                 __builtin_bit_cast(uint32_t, l23)};
+      p_hi = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+      p_lo = u32x2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
     }
 
-    // 4) O^T += V^T P^T, one MFMA per 16 rows of d
+    // 4) O^T += V^T P^T: per 16 rows of d, two 16x16x16 MFMAs (hi and lo
+    //    parts of P) whose A operand is the 8-byte V^T cell of 4 tokens
+    u32x2 cell[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int d = 16 * n + lo16;
-      const u32x2 cell = sm.vt[wave][d ^ ((d >> 3) & 7)][q4];
-      acc[n] = mfma_16x16x32<CT>(u32x4{cell[0], cell[1], cell[0], cell[1]}, pb, acc[n]);
+      cell[n] = sm.vt[wave][d ^ ((d >> 3) & 7)][q4];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16<CT>(cell[n], p_hi, acc[n]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16<CT>(cell[n], p_lo, acc[n]);
+    mfma_guard();
     compiler_fence();
   };
 
@@ -485,7 +531,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     const int t0 = wb + c0;             // its first tile
     // Lane j holds the physical block of tile t0 + j (clamped into the chunk,
     // so only table entries of blocks the context covers are read).
-    const int ids = bt_row[((t0 + min(lane, cn - 1)) * kTileTokens) / p.block_size];
+    const int ids = bt_row[(t0 + min(lane, cn - 1)) >> p.tile_shift];
 
     auto load_tile = [&](Tile& r, int j) {  // j: tile of the chunk, 0 <= j < cn (wave-uniform)
       const int tok0 = (t0 + j) * kTileTokens;
@@ -494,7 +540,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       phys = ok ? phys : 0;
       const int rem = it.ctx - tok0;
       r.lim = ok ? (rem < kTileTokens ? rem : kTileTokens) : 0;
-      const size_t off = (size_t)phys * block_bytes + (size_t)(tok0 % p.block_size) * ROW;
+      const int sub = (t0 + j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
+      const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
       const uint8_t* kp = kbase + off;
 #pragma unroll
       for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kp + c * 64);
@@ -520,7 +567,12 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     // Ring of NBUF buffers: tile i + NBUF - 1 is loaded while tile i is computed.
     Tile buf[NBUF];
 #pragma unroll
-    for (int b = 0; b < NBUF - 1; ++b) load_tile(buf[b], min(b, cn - 1));
+    for (int b = 0; b < NBUF - 1; ++b) {
+      load_tile(buf[b], min(b, cn - 1));
+      // keep the tiles' loads in ring order, so that waiting for the oldest
+      // tile never waits for a younger one
+      __builtin_amdgcn_sched_barrier(0);
+    }
     for (int i = 0; i < cn; i += NBUF) {
 #pragma unroll
       for (int b = 0; b < NBUF; ++b) {
@@ -697,6 +749,8 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.max_blocks_per_seq = a.max_blocks_per_seq;
   p.num_splits = a.num_splits;
   p.tiles_per_split = a.tiles_per_split;
+  p.tile_shift = 0;
+  while ((kTileTokens << p.tile_shift) < a.block_size) ++p.tile_shift;
   p.units = a.num_seqs * a.h_kv;
   p.scale_log2 = a.scale_log2;
   p.v_scale = a.v_scale;

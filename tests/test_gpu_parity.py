@@ -63,8 +63,11 @@ def test_vector_path(types, d, group, bs):
 @pytest.mark.parametrize("types", [("bf16", "bf16", "bf16"), ("bf16", "fp8", "bf16"), ("f32", "f32", "f32")],
                          ids=lambda t: "-".join(t))
 @pytest.mark.parametrize("splits", [1, 2, 3, 5, 16, 64])
-def test_forced_splits(types, splits):
-    wl = small(16, 2, 128, 16, *types, contexts=(1, 33, 250, 600, 1000, 1023, 7, 511), seed=11)
+@pytest.mark.parametrize("d", [64, 128])
+def test_forced_splits(types, splits, d):
+    """Few splits make every wave walk many tiles in a row (the accumulators
+    carry across tiles); many splits leave waves with one tile or none."""
+    wl = small(16, 2, d, 16, *types, contexts=(1, 33, 250, 600, 1000, 1023, 7, 511), seed=11)
     check_step(wl, num_splits=splits, label=f"{wl.name}-splits{splits}")
 
 
