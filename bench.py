@@ -9,9 +9,12 @@ attention runs over it.  Each layer has its own pool of 2,457 blocks (the
 
 value = KV bytes a step must read (sum over sequences of context_len x 2 x
 h_kv x head_dim x 2 B, x 80 layers) / step time, in GB/s.
-roofline = the decode kernel alone: the same bytes per launch / its average
-launch duration (HIP events around each launch, on its stream).
-cpu_baseline = the float64 oracle on a bounded sample of one layer.
+roofline = the decode kernel alone: the same bytes per launch / its mean
+launch duration (HIP events on its stream around back-to-back launches over
+the layer pools); traffic = HBM bytes per launch from rocprofv3 counters,
+reported only while the kernel source is the one they were taken on.
+cpu_baseline = the float64 oracle on whole layer calls, repeated for a
+bounded time on the host.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
 """
@@ -31,6 +34,29 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "gqa70b-bf16-47x825"
 
 
+# HBM bytes per decode launch from rocprofv3 counters (FETCH_SIZE x 2 +
+# WRITE_SIZE: on a 1 GiB device copy FETCH_SIZE reads half the bytes read and
+# WRITE_SIZE all the bytes written), valid only for the kernel source they
+# were taken on (its SHA-256) and the workload / split count they ran.
+MEASURED_TRAFFIC = {
+    # (kernel source sha256, workload, num_splits): bytes per launch
+    ("5a402181d5befa13a295b62a1eda343627f7a6380cf93aae23ffbac5156261ba", "gqa70b-bf16-47x825", 1): 162719334,
+}
+
+
+def kernel_source_sha256():
+    import hashlib
+    path = os.path.join(ROOT, "paged_kv_cache_431_amd", "csrc", "paged_decode.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload, num_splits):
+    """Counter-measured HBM bytes per launch, or None if the decode kernel
+    changed since they were taken (or they were never taken for this case)."""
+    return MEASURED_TRAFFIC.get((kernel_source_sha256(), workload, int(num_splits)))
+
+
 def kv_bytes_per_call(plan, unique=True):
     """Algorithmic K+V bytes one decode call reads: used tokens only."""
     import workloads
@@ -44,8 +70,9 @@ def kv_bytes_per_call(plan, unique=True):
 
 
 def cpu_baseline(plan, rp, tensors, budget_s):
-    """Time the oracle (scatter + attention, one sequence at a time) on as many
-    sequences of one layer as fit in about budget_s seconds."""
+    """Time the oracle on whole layer calls of the workload (the scatter of the
+    new tokens, then float64 attention one sequence at a time), repeating the
+    layer until about budget_s seconds of host work are done."""
     import numpy as np
     import torch
 
@@ -58,19 +85,21 @@ def cpu_baseline(plan, rp, tensors, budget_s):
     to_np = lambda x: x.view(bits[x.dtype][0]).cpu().numpy().view(bits[x.dtype][1])
     q, kc, vc = to_np(tensors.q), to_np(tensors.k_cache), to_np(tensors.v_cache)
     nk, nv = to_np(tensors.new_k), to_np(tensors.new_v)
-    per_token = 2 * wl.h_kv * wl.head_dim * {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    per_call = kv_bytes_per_call(plan)
+    done_calls, done_seqs, done_bytes = 0, 0, 0
     t0 = time.perf_counter()
-    kc2, vc2 = oracle.scatter.reshape_and_cache(nk, nv, kc, vc, rp.slot_mapping, in_dtype=wl.new_dtype,
-                                                kv_dtype=wl.kv_dtype, block_size=wl.block_size,
-                                                k_scale=tensors.k_scale, v_scale=tensors.v_scale)
-    done_bytes, done_seqs = 0, 0
-    for s in range(wl.num_seqs):
-        oracle.attention.paged_attention_decode(q, kc2, vc2, rp.block_tables, plan.context_lens, q_dtype=wl.q_dtype,
-                                                kv_dtype=wl.kv_dtype, block_size=wl.block_size,
-                                                scale=1.0 / math.sqrt(wl.head_dim), k_scale=tensors.k_scale,
-                                                v_scale=tensors.v_scale, seqs=[s])
-        done_seqs += 1
-        done_bytes += int(plan.context_lens[s]) * per_token
+    while True:
+        kc2, vc2 = oracle.scatter.reshape_and_cache(nk, nv, kc, vc, rp.slot_mapping, in_dtype=wl.new_dtype,
+                                                    kv_dtype=wl.kv_dtype, block_size=wl.block_size,
+                                                    k_scale=tensors.k_scale, v_scale=tensors.v_scale)
+        for s in range(wl.num_seqs):
+            oracle.attention.paged_attention_decode(q, kc2, vc2, rp.block_tables, plan.context_lens,
+                                                    q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype,
+                                                    block_size=wl.block_size, scale=1.0 / math.sqrt(wl.head_dim),
+                                                    k_scale=tensors.k_scale, v_scale=tensors.v_scale, seqs=[s])
+        done_calls += 1
+        done_seqs += wl.num_seqs
+        done_bytes += per_call
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
@@ -81,8 +110,8 @@ def cpu_baseline(plan, rp, tensors, budget_s):
         threads = 1
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "seqs_per_s": round(done_seqs / dt, 3), "host_cpus": os.cpu_count(),
-            "sample": f"{done_seqs} of {wl.num_seqs} sequences of one layer of {wl.name} "
-                      f"(scatter of all new tokens + float64 attention, one sequence at a time), {dt:.1f} s"}
+            "sample": f"{done_calls} repeats of one layer call of {wl.name} ({wl.num_seqs} sequences: scatter of the "
+                      f"new tokens, then float64 attention one sequence at a time), {dt:.1f} s"}
 
 
 def main():
@@ -93,8 +122,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=80)
     ap.add_argument("--splits", type=int, default=0, help="force the decode split count (0 = library's choice)")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only copy a buffer of this many MiB a few times (calibrates byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -108,6 +139,17 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
+    if args.copy_probe_mib:
+        # A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
+        # readings per dispatch give the scale of those counters.
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 4}), flush=True)
+        return
     wl = workloads.get(args.workload)
     plan = workloads.plan(wl)
     bm = pkv.BlockManager(plan.num_blocks, wl.block_size, plan.free_order)
@@ -149,8 +191,19 @@ def main():
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
 
-    # The decode kernel alone: an event pair around every launch.
+    # The decode kernel alone: L back-to-back launches (one per layer pool)
+    # between one event pair on the kernel's stream, repeated; the mean launch
+    # duration is the total over the launches.  An event pair around each
+    # single launch is also kept (it adds the event and dispatch overhead).
     reps = max(1, min(5, args.steps))
+    batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in batch:
+        a.record(stream)
+        for decode in decodes:
+            decode()
+        b.record(stream)
+    torch.cuda.synchronize()
+    mean_launch_ms = sum(a.elapsed_time(b) for a, b in batch) / (reps * L)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * L)]
     for r in range(reps):
         for l, decode in enumerate(decodes):
@@ -160,7 +213,6 @@ def main():
             b.record(stream)
     torch.cuda.synchronize()
     launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    mean_launch_ms = sum(launch_ms) / len(launch_ms)
 
     per_call = kv_bytes_per_call(plan)
     step_bytes = per_call * L
@@ -189,10 +241,12 @@ def main():
         "seqs_per_s": round(wl.num_seqs / (ms_step * 1e-3 / L), 1),
         "decode_steps_per_s": round(1000.0 / ms_step, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name, n_splits),
                      "kernel": "decode_mfma_kernel" if wl.kv_dtype != "f32" else "decode_vector_kernel",
                      "mean_launch_us": round(mean_launch_ms * 1e3, 3),
-                     "median_launch_us": round(launch_ms[len(launch_ms) // 2] * 1e3, 3)},
+                     "isolated_launch_median_us": round(launch_ms[len(launch_ms) // 2] * 1e3, 3),
+                     "algorithmic_bytes_per_launch": per_call},
     }
     if not args.no_cpu_baseline:
         del pools, decodes, scatters, layer_calls
