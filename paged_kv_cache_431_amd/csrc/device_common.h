@@ -12,6 +12,7 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(4))) short v4i16;
 
 // Element type tags (match pkv_dtype).
 enum Dt : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };

@@ -348,10 +348,12 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int NBUF = Tile::NBUF;
   constexpr int NK = D / 32;  // MFMA k-steps for the scores
   constexpr int NT = D / 16;  // 16-row output tiles of the PV product
-  constexpr int DW = D / 16;  // d values per lane in the V transpose
+  constexpr int VCH = D / 8;  // 16-byte chunks in a 16-bit V row
 
   __shared__ union {
-    u32x2 vt[kDecodeWaves][D][4];  // per-wave V^T tile: [d (swizzled)][token quad] of 4 x 16-bit
+    // per-wave V tile of 16 tokens in its natural [token][d] layout, 16-bit
+    // elements, 16-byte chunks of each row XOR-swizzled by the row
+    u32x4 vtile[kDecodeWaves][kTileTokens * VCH];
     MergeSmem<D> merge;
   } sm;
 
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
     mfma_guard();
 
-    // 2) V -> LDS as V^T[d][token quad]; masked rows are zeroed first
+    // 2) V -> LDS in its natural layout; masked rows are zeroed first
     const bool partial = lim < kTileTokens;
     if (partial) {
 #pragma unroll
@@ -430,28 +432,30 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
           for (int w = 0; w < VDW; ++w) r.v[rr][w] = 0u;
         }
     }
-    if constexpr (KV == kFP8) {
-      // one dword (4 elements) of each of the 4 rows at a time: element
-      // e = 4 * w + x of row rr is byte x of dword w
+    // Row t of the tile, 16-byte chunk c sits at chunk c ^ swz(t) of row t:
+    // the transposed reads below then touch all banks evenly.
+    auto vt_chunk = [&](int t, int c) { return t * VCH + (c ^ ((t & (VCH / 2 - 1)) << 1)); };
+    u32x4* vt = sm.vtile[wave];
 #pragma unroll
-      for (int w = 0; w < VDW; ++w) {
-        float f[4][4];
+    for (int rr = 0; rr < 4; ++rr) {
+      const int t = 4 * q4 + rr;  // this lane holds d = lo16 * D/16 ... of row t
+      uint32_t w16[D / 32];       // those D/16 elements as 16-bit pairs
+      if constexpr (KV == kFP8) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) fp8x4_to_f32(r.v[rr][w], f[rr]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int d = lo16 * DW + 4 * w + x;
-          sm.vt[wave][d ^ ((d >> 3) & 7)][q4] =
-              u32x2{pack_exact<CT>(f[0][x], f[1][x]), pack_exact<CT>(f[2][x], f[3][x])};
+        for (int w = 0; w < VDW; ++w) {
+          float f[4];
+          fp8x4_to_f32(r.v[rr][w], f);
+          w16[2 * w] = pack_exact<CT>(f[0], f[1]);
+          w16[2 * w + 1] = pack_exact<CT>(f[2], f[3]);
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int e = 0; e < DW; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-        const int d = lo16 * DW + e;
-        sm.vt[wave][d ^ ((d >> 3) & 7)][q4] = u32x2{__builtin_amdgcn_perm(r.v[1][e >> 1], r.v[0][e >> 1], sel),
-                                                     __builtin_amdgcn_perm(r.v[3][e >> 1], r.v[2][e >> 1], sel)};
+        for (int w = 0; w < VDW; ++w) w16[w] = r.v[rr][w];
+      }
+      if constexpr (D == 128) {
+        vt[vt_chunk(t, lo16)] = u32x4{w16[0], w16[1], w16[2], w16[3]};
+      } else {
+        reinterpret_cast<u32x2*>(vt + vt_chunk(t, lo16 >> 1))[lo16 & 1] = u32x2{w16[0], w16[1]};
       }
     }
     compiler_fence();
@@ -511,11 +515,20 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
 
     // 4) O^T += V^T P^T: per 16 rows of d, two 16x16x16 MFMAs (hi and lo
     //    parts of P) whose A operand is the 8-byte V^T cell of 4 tokens
+    // A operands by transposing reads: lane (4k + m) of each 16-lane group
+    // points at 4 elements d = 16n + 4m .. +3 of token 4*q4 + k, and lane j
+    // receives element j of those 4 tokens' rows, i.e. V^T[16n + j][4*q4 .. +3]
     u32x2 cell[NT];
+    {
+      const int t = 4 * q4 + (lo16 >> 2);
+      const int m = lo16 & 3;
+      typedef __attribute__((address_space(3))) char lds_char;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int d = 16 * n + lo16;
-      cell[n] = sm.vt[wave][d ^ ((d >> 3) & 7)][q4];
+      for (int n = 0; n < NT; ++n) {
+        lds_char* a = (lds_char*)(vt + vt_chunk(t, 2 * n + (m >> 1))) + 8 * (m & 1);
+        cell[n] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                (__attribute__((address_space(3))) v4i16*)a));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
