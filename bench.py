@@ -248,6 +248,25 @@ def main():
                      "isolated_launch_median_us": round(launch_ms[len(launch_ms) // 2] * 1e3, 3),
                      "algorithmic_bytes_per_launch": per_call},
     }
+    # copy-on-write block copy: disjoint (src, dst) block pairs of one layer pool
+    n_pairs = min(1024, plan.num_blocks // 2)
+    perm = np.random.default_rng(7).permutation(plan.num_blocks)
+    pairs = torch.from_numpy(np.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], axis=1).astype(np.int32)).to(dev)
+    t0 = pools[0]
+    for _ in range(3):
+        pkv.pkv_copy_blocks(t0.k_cache, t0.v_cache, pairs, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        pkv.pkv_copy_blocks(t0.k_cache, t0.v_cache, pairs, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = a.elapsed_time(b) / 10
+    block_bytes = wl.h_kv * wl.block_size * wl.head_dim * workloads.ELEMENT_BYTES[wl.kv_dtype]
+    moved = n_pairs * 2 * block_bytes * 2  # K and V blocks, each read once and written once
+    result["copy_blocks"] = {"pairs": n_pairs, "block_bytes_per_pool": block_bytes, "us_per_call": round(copy_ms * 1e3, 3),
+                             "read_plus_write_GBps": round(moved / (copy_ms * 1e-3) / 1e9, 1),
+                             "frac_of_hbm_peak": round(moved / (copy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
         del pools, decodes, scatters, layer_calls
         torch.cuda.empty_cache()

@@ -153,6 +153,29 @@ int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype,
                           int h_kv, int head_dim, int block_size, int num_blocks, void* stream);
 
 /* ------------------------------------------------------------------------
+ * copy_blocks: the block copy of copy-on-write.
+ *
+ * Sequences share prefix blocks by reference; a sequence that appends into a
+ * shared block that is only partly filled moves onto a fresh block first
+ * ("Paged KV Cache" tutorial, section "Block Tables and Sharing"; "KV cache
+ * and PagedAttention in serving", section "The bonus: sharing via
+ * copy-on-write").  pkv_bm_append reports that move as (cow_src, cow_dst);
+ * this call copies block src to block dst, every KV head and slot, in both
+ * pools, so that the sequence's tokens are in its new block before its new
+ * token is written (call it before pkv_reshape_and_cache on the same stream).
+ *   block_pairs  [num_pairs, 2] int32 in device memory: (src, dst) per row.
+ *                All rows see the pools as they were before the call: a
+ *                block must not be both a source and a destination, and a
+ *                destination must not repeat (caller error, not checked).
+ *                A row with an id outside [0, num_blocks) is skipped.
+ *   k_cache ...  [NB, Hkv, B, D] in kv_dtype; h_kv * B * D * element bytes
+ *                must be a multiple of 16.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
+ * ------------------------------------------------------------------------ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, const int32_t* block_pairs, int num_pairs,
+                    int h_kv, int head_dim, int block_size, int num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block manager (no device memory; pure host bookkeeping)
  *
  * Blocks are handed out only as a sequence grows ("AI Engineering

@@ -25,6 +25,7 @@ Modules
   codecs     -- element codecs (bf16 / f16 / f32 / fp8 e4m3) decoded from bits.
   attention  -- paged decode attention: resolve block tables, textbook softmax.
   scatter    -- reshape_and_cache: write each new token's K/V into its slot.
+  copy       -- copy_blocks: the block copy of copy-on-write.
   allocator  -- block manager: FIFO free list, refcounts, fork, copy-on-write.
   capacity   -- the pages' sizing arithmetic (bytes/token, slots, blocks).
 
@@ -33,4 +34,4 @@ Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 library routine, or brute force; none is "parity unpinned".
 """
 
-from . import allocator, attention, capacity, codecs, scatter  # noqa: F401
+from . import allocator, attention, capacity, codecs, copy, scatter  # noqa: F401

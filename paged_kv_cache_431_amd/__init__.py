@@ -11,6 +11,7 @@ HIP stream to the C ABI declared in include/pkv.h (same function names).
 
   pkv_paged_attention_decode   paged decode attention (one launch)
   pkv_reshape_and_cache        write new tokens' K/V into their slots
+  pkv_copy_blocks              copy blocks (src -> dst) in both pools: copy-on-write
   pkv_decode_workspace_bytes   workspace size for a decode call
   pkv_decode_num_splits        split count the library will use
   BlockManager                 the host block manager (pkv_bm_*)
@@ -61,6 +62,7 @@ def lib():
                                                c_p, c_sz, c_p]),
         "pkv_reshape_and_cache": (c_int, [c_p, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_int, c_int, c_int,
                                           c_int, c_int, c_p]),
+        "pkv_copy_blocks": (c_int, [c_p, c_p, c_int, c_p, c_int, c_int, c_int, c_int, c_int, c_p]),
         "pkv_bm_create": (c_int, [c_i32, c_i32, p_i32, ctypes.POINTER(c_p)]),
         "pkv_bm_destroy": (None, [c_p]),
         "pkv_bm_append": (c_int, [c_p, c_i32, c_i32, p_i64, p_i32, p_i32]),
@@ -213,6 +215,21 @@ def pkv_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, *, k_scale
         _dev_ptr(v_cache, "v_cache"), dtype_code(k_cache), float(k_scale), float(v_scale),
         _dev_ptr(slot_mapping, "slot_mapping"), T, h_kv, D, B, NB, _stream(stream))
     _check(st, "pkv_reshape_and_cache")
+
+
+def pkv_copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
+    """Copy block src -> dst for every row of block_pairs [n, 2] (int32, on
+    the GPU) in both pools (the copy of copy-on-write)."""
+    import torch
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must have one shape and dtype")
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise TypeError("block_pairs must be int32 [n, 2]")
+    NB, h_kv, B, D = k_cache.shape
+    st = lib().pkv_copy_blocks(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), dtype_code(k_cache),
+                               _dev_ptr(block_pairs, "block_pairs"), block_pairs.shape[0], h_kv, D, B, NB,
+                               _stream(stream))
+    _check(st, "pkv_copy_blocks")
 
 
 class BlockManager:

@@ -168,4 +168,18 @@ int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype, void
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
+int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, const int32_t* block_pairs, int num_pairs, int h_kv,
+                    int head_dim, int block_size, int num_blocks, void* stream) {
+  if (num_pairs < 0 || h_kv < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1) return PKV_EINVAL;
+  if (!valid_dtype(kv_dtype)) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PKV_EINVAL;
+  static const int kElementBytes[4] = {4, 2, 2, 1};
+  const int64_t block_bytes = (int64_t)h_kv * block_size * head_dim * kElementBytes[kv_dtype];
+  if (block_bytes % 16 != 0) return PKV_EUNSUPPORTED;
+  const hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, block_bytes, num_blocks,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
 }  // extern "C"

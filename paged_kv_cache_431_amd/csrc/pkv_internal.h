@@ -54,4 +54,7 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, int in_d
                                     int num_tokens, int h_kv, int head_dim, int block_size, int num_blocks,
                                     hipStream_t stream);
 
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int64_t block_bytes,
+                              int num_blocks, hipStream_t stream);
+
 }  // namespace pkv

@@ -100,3 +100,18 @@ def test_reshape_and_cache_rejects_bad_scalars():
     assert call(d=12) == pkv.PKV_EUNSUPPORTED
     assert call(inb=2, kv=1) == pkv.PKV_EUNSUPPORTED
     assert call(T=0) == pkv.PKV_OK
+
+
+def test_copy_blocks_rejects_bad_scalars():
+    L = pkv.lib()
+    P = ctypes.c_void_p
+    call = lambda **o: L.pkv_copy_blocks(P(o.get("k", 1)), P(1), o.get("kv", 2), P(o.get("pairs", 1)),
+                                         o.get("n", 3), o.get("hkv", 2), o.get("d", 128), o.get("bs", 16),
+                                         o.get("nb", 10), None)
+    assert call(n=-1) == pkv.PKV_EINVAL
+    assert call(pairs=None) == pkv.PKV_EINVAL
+    assert call(k=None) == pkv.PKV_EINVAL
+    assert call(kv=9) == pkv.PKV_EINVAL
+    assert call(nb=0) == pkv.PKV_EINVAL
+    assert call(kv=3, hkv=1, d=3, bs=1) == pkv.PKV_EUNSUPPORTED   # a 3-byte block
+    assert call(n=0) == pkv.PKV_OK                                # nothing to do, nothing launched
