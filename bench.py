@@ -121,6 +121,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=80)
+    ap.add_argument("--block-size", type=int, default=0, help="tokens per block (0: the workload's own, 16)")
     ap.add_argument("--splits", type=int, default=0, help="force the decode split count (0 = library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,6 +152,11 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 4}), flush=True)
         return
     wl = workloads.get(args.workload)
+    if args.block_size and args.block_size != wl.block_size:
+        # same byte budget per layer pool, blocks of another size
+        blocks = wl.num_blocks * wl.block_size // args.block_size if wl.num_blocks else 0
+        wl = workloads.replace(wl, name=f"{wl.name}-b{args.block_size}", block_size=args.block_size,
+                               num_blocks=blocks)
     plan = workloads.plan(wl)
     bm = pkv.BlockManager(plan.num_blocks, wl.block_size, plan.free_order)
     rp = workloads.replay(plan, bm)

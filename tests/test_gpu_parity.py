@@ -157,3 +157,13 @@ def test_split_count_changes_stay_within_tolerance():
     ref = c.oracle_decode()
     for n in (1, 2, 7, 30):
         assert_close(c.decode(num_splits=n), ref, "fp8", label=f"splits={n}")
+
+
+def test_units_not_a_multiple_of_the_compute_units():
+    """300 units (75 sequences x 4 KV heads) of mixed lengths: more units
+    than compute units, not a whole multiple of them; every output row."""
+    rng = np.random.default_rng(23)
+    contexts = tuple(int(c) for c in rng.integers(1, 300, size=75))
+    wl = workloads.Workload("units-75x4", 75, 16, 4, 128, 16, "bf16", "bf16", "bf16", 29, contexts=contexts,
+                            extra_blocks=7)
+    check_step(wl, label="units-75x4")
