@@ -40,7 +40,7 @@ DEFAULT_WORKLOAD = "gqa70b-bf16-47x825"
 # were taken on (its SHA-256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("5a402181d5befa13a295b62a1eda343627f7a6380cf93aae23ffbac5156261ba", "gqa70b-bf16-47x825", 1): 162719334,
+    ("00e218a4533513a0179d5e27618465151b12c228accc59e868b79ba58856d21d", "gqa70b-bf16-47x825", 1): 162715853,
 }
 
 
