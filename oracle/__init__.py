@@ -23,7 +23,8 @@ and the section on it:
 
 Modules
   codecs     -- element codecs (bf16 / f16 / f32 / fp8 e4m3) decoded from bits.
-  attention  -- paged decode attention: resolve block tables, textbook softmax.
+  attention  -- paged attention: resolve block tables, textbook softmax; decode
+                (one new token) and several new tokens with a causal mask.
   scatter    -- reshape_and_cache: write each new token's K/V into its slot.
   copy       -- copy_blocks: the block copy of copy-on-write.
   allocator  -- block manager: FIFO free list, refcounts, fork, copy-on-write.

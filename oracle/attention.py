@@ -111,3 +111,69 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, *,
             kvh = kv_head_of(g, h_q, h_kv)
             out[s, g] = attend(q_s[g], keys[kvh], vals[kvh], scale)
     return out
+
+
+# ---------------------------------------------------------------- several new query tokens
+#
+# What the pages fix
+#   * every token already processed keeps its K and V so that the tokens after
+#     it can attend to them ([UD] intro): attention runs forward in position,
+#     a token sees the positions before it;
+#   * a prompt whose prefix is already cached recomputes only its trailing
+#     tokens over that prefix ([AF] "Beyond paging: radix trees and continuous
+#     batching"), and speculative decoding adds lookahead tokens past the
+#     committed ones ([OT] "Internal Fragmentation"): one step can bring
+#     several new tokens of one sequence.
+# Readings of what the pages leave open
+#   * the m new tokens of a sequence are the last m of its context_len cached
+#     tokens (their K/V already written), so new token i sits at position
+#     context_len - m + i;
+#   * a token attends to its own position too (its K/V are cached like the
+#     others) and to no later one;
+#   * a token with no position to attend to (more new tokens than cached
+#     ones) gets 0, as an empty context does for decode.
+
+
+def causal_visible(context_len: int, num_new: int, i: int) -> int:
+    """How many positions new token i (of num_new) attends to: [0, ctx - m + i]."""
+    return max(0, context_len - num_new + i + 1)
+
+
+def paged_attention_multi(q, k_cache, v_cache, block_tables, context_lens, query_start, *,
+                          q_dtype, kv_dtype, block_size, scale=None, k_scale=1.0, v_scale=1.0, seqs=None):
+    """Float64 output [num_query_tokens, h_q, head_dim] for several new tokens per sequence.
+
+    q: [T, h_q, head_dim] stored bits; rows query_start[s] .. query_start[s+1]-1
+    are the new tokens of sequence s in order.  Rows of sequences not in
+    `seqs` (and rows no sequence owns) are NaN.
+    """
+    T, h_q, head_dim = q.shape
+    num_seqs = len(context_lens)
+    h_kv = k_cache.shape[1]
+    if h_q % h_kv != 0:
+        raise ValueError("h_q must be a multiple of h_kv")
+    if k_cache.shape[2] != block_size:
+        raise ValueError("k_cache block dimension must equal block_size")
+    if len(query_start) != num_seqs + 1:
+        raise ValueError("query_start needs num_seqs + 1 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    max_blocks = block_tables.shape[1]
+    out = np.full((T, h_q, head_dim), np.nan, dtype=np.float64)
+    for s in (range(num_seqs) if seqs is None else seqs):
+        q0, q1 = int(query_start[s]), int(query_start[s + 1])
+        if not 0 <= q0 <= q1 <= T:
+            raise ValueError(f"query rows [{q0}, {q1}) of sequence {s} out of range")
+        m = q1 - q0
+        ctx = int(context_lens[s])
+        if not 0 <= ctx <= max_blocks * block_size:
+            raise ValueError(f"context length {ctx} of sequence {s} out of range")
+        keys = resolve_sequence(k_cache, block_tables[s], ctx, block_size, kv_dtype, k_scale)
+        vals = resolve_sequence(v_cache, block_tables[s], ctx, block_size, kv_dtype, v_scale)
+        for i in range(m):
+            n = causal_visible(ctx, m, i)
+            q_i = bits_to_f64(q[q0 + i], q_dtype)
+            for g in range(h_q):
+                kvh = kv_head_of(g, h_q, h_kv)
+                out[q0 + i, g] = attend(q_i[g], keys[kvh, :n], vals[kvh, :n], scale)
+    return out

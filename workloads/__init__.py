@@ -257,6 +257,16 @@ def make_tensors(p: Plan, rp: Replay, device="cpu", poison=True, pool_seed_offse
     return Tensors(q, kc, vc, nk, nv, k_scale, v_scale)
 
 
+def multi_queries(wl: Workload, new_tokens, device="cpu"):
+    """Query rows for several new tokens per sequence: q [sum(new_tokens),
+    h_q, head_dim] in q_dtype (seeded N(0,1), its own stream) and the int32
+    row offsets query_start [num_seqs + 1]."""
+    dev = torch.device(device)
+    qs = np.concatenate([[0], np.cumsum(np.asarray(new_tokens, dtype=np.int64))]).astype(np.int32)
+    q = _randn((int(qs[-1]), wl.h_q, wl.head_dim), _generator(wl.seed, 7, dev), dev).to(TORCH_DTYPES[wl.q_dtype])
+    return q, qs
+
+
 def _to_fp8(x, scale, chunk_rows=512):
     out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     s = torch.tensor(scale, dtype=torch.float32, device=x.device)
