@@ -13,6 +13,10 @@ roofline = the decode kernel alone: the same bytes per launch / its mean
 launch duration (HIP events on its stream around back-to-back launches over
 the layer pools); traffic = HBM bytes per launch from rocprofv3 counters,
 reported only while the kernel source is the one they were taken on.
+copy_blocks = the block copy of copy-on-write (1,024 block pairs, K and V).
+multi_query = a speculative step: 4 new query tokens per sequence (the last 4
+positions of each context, causal), the same pools; GB/s counts each cached
+K/V byte once.
 cpu_baseline = the float64 oracle on whole layer calls, repeated for a
 bounded time on the host.
 
@@ -38,6 +42,9 @@ DEFAULT_WORKLOAD = "gqa70b-bf16-47x825"
 # WRITE_SIZE: on a 1 GiB device copy FETCH_SIZE reads half the bytes read and
 # WRITE_SIZE all the bytes written), valid only for the kernel source they
 # were taken on (its SHA-256) and the workload / split count they ran.
+# Lookahead tokens per sequence of the speculative step measured beside decode.
+MULTI_TOKENS = 4
+
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
     ("00e218a4533513a0179d5e27618465151b12c228accc59e868b79ba58856d21d", "gqa70b-bf16-47x825", 1): 162715853,
@@ -273,8 +280,37 @@ def main():
     result["copy_blocks"] = {"pairs": n_pairs, "block_bytes_per_pool": block_bytes, "us_per_call": round(copy_ms * 1e3, 3),
                              "read_plus_write_GBps": round(moved / (copy_ms * 1e-3) / 1e9, 1),
                              "frac_of_hbm_peak": round(moved / (copy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # several new query tokens per sequence: a speculative step that verifies
+    # MULTI_TOKENS lookahead tokens, the last MULTI_TOKENS positions of each
+    # context, over the same layer pools and tables (causal within them)
+    m = MULTI_TOKENS
+    qm, qs = workloads.multi_queries(wl, [m] * wl.num_seqs, device=dev)
+    qs_t = torch.from_numpy(qs).to(dev)
+    out_m = torch.empty(qm.shape[0], wl.h_q, wl.head_dim, dtype=torch.float32, device=dev)
+    ws_m = pkv.make_multi_workspace(wl.num_seqs, wl.h_q, wl.h_kv, wl.head_dim, wl.block_size, m,
+                                    plan.max_context_len, 0, device=dev)
+    multis = [pkv.prepare_paged_attention_multi(out_m, qm, t.k_cache, t.v_cache, tables, lens, qs_t, max_query_len=m,
+                                                max_context_len=plan.max_context_len, workspace=ws_m,
+                                                k_scale=t.k_scale, v_scale=t.v_scale, stream=stream) for t in pools]
+    for call in multis:
+        call()
+    batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in batch:
+        a.record(stream)
+        for call in multis:
+            call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    multi_ms = sum(a.elapsed_time(b) for a, b in batch) / (reps * L)
+    result["multi_query"] = {
+        "new_tokens_per_seq": m, "query_rows": int(qm.shape[0]),
+        "num_splits": pkv.pkv_multi_num_splits(wl.num_seqs, wl.h_q, wl.h_kv, wl.head_dim, wl.block_size, m,
+                                               plan.max_context_len, 0),
+        "mean_launch_us": round(multi_ms * 1e3, 3),
+        "kv_GBps": round(per_call / (multi_ms * 1e-3) / 1e9, 2),
+        "frac_of_hbm_peak": round(per_call / (multi_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
-        del pools, decodes, scatters, layer_calls
+        del pools, decodes, scatters, layer_calls, multis
         torch.cuda.empty_cache()
         fresh = workloads.make_tensors(plan, rp, device=dev, poison=False, pool_seed_offset=0)  # untouched by HIP
         result["cpu_baseline"] = cpu_baseline(plan, rp, fresh, args.cpu_budget)

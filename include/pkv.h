@@ -130,6 +130,60 @@ int pkv_paged_attention_decode(void* out, int out_dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Paged attention for several new query tokens per sequence (a chunk of a
+ * prompt recomputed over a cached prefix, or the lookahead tokens of
+ * speculative decoding), with a causal mask.
+ *
+ * Every token already processed keeps its K/V so that later tokens can
+ * attend to it ("AI Engineering Visualised: KV cache", intro); a prompt
+ * whose prefix is found in the cache recomputes only its trailing tokens
+ * over that prefix ("KV cache and PagedAttention in serving", section
+ * "Beyond paging: radix trees and continuous batching"); speculative
+ * decoding places lookahead tokens in slots past the committed ones ("Paged
+ * KV Cache" tutorial, section "Internal Fragmentation").
+ *
+ * Shapes (T = num_query_tokens, others as for decode):
+ *   out, q        [T, Hq, D]   rows query_start[s] .. query_start[s+1]-1 are
+ *                              the m_s new tokens of sequence s, in order
+ *   query_start   [S + 1] int32, device memory, non-decreasing; entries are
+ *                              clamped into [0, T] and m_s to max_query_len,
+ *                              so no row outside [0, T) is read or written
+ *                              (rows cut off this way are left untouched)
+ *   k_cache ...   as for decode; context_lens[s] counts the cached tokens
+ *                              INCLUDING the m_s new ones, whose K/V must
+ *                              already be in their slots (reshape_and_cache)
+ * Semantics: query token i of sequence s sits at position
+ *   p = ctx_s - m_s + i and attends to positions [0, p] (itself included):
+ *   out[q0 + i, g, :] = sum_{t <= p} softmax_t(scale q . K_s[h, t]) V_s[h, t]
+ * with q0 = query_start[s] and h = g / (Hq / Hkv).  A row with p < 0 (more
+ * new tokens than cached ones) attends over nothing and gets 0.  m_s = 1 and
+ * query_start[s] = s give exactly the decode call.
+ *
+ * Supported: the matrix-core combinations of decode (16-bit or FP8 caches,
+ * B a multiple of 16 with B / 16 a power of two, D in {64, 128},
+ * 1 <= Hq / Hkv <= 16); others return PKV_EUNSUPPORTED.  The (query token,
+ * head) rows of one (sequence, KV head) are processed 16 at a time.
+ * max_query_len: 1 <= max_query_len <= 2^24, an upper bound of every m_s.
+ * Workspace: pkv_multi_workspace_bytes(...) bytes for the same sizes, zeroed
+ *   before first use and reusable afterwards, as for decode.
+ * Errors: PKV_EINVAL (as decode, plus NULL query_start with S > 0, T < 0,
+ *   max_query_len out of range), PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP.
+ * ------------------------------------------------------------------------ */
+size_t pkv_multi_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
+                                 int max_context_len, int num_splits);
+
+/* The split count the library will use for these sizes (>= 1), or 0 if invalid. */
+int pkv_multi_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
+                         int max_context_len, int num_splits);
+
+int pkv_paged_attention_multi(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
+                              int num_query_tokens, int max_query_len, const void* k_cache, const void* v_cache,
+                              int kv_dtype, float k_scale, float v_scale, const int32_t* block_tables,
+                              const int32_t* context_lens, int num_seqs, int h_q, int h_kv, int head_dim,
+                              int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+                              float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * reshape_and_cache: write each new token's K and V into its slot.
  *
  * A slot is physical_block * block_size + offset_in_block; token i's K for

@@ -10,10 +10,13 @@ check their shapes and dtypes, and pass raw device pointers plus the current
 HIP stream to the C ABI declared in include/pkv.h (same function names).
 
   pkv_paged_attention_decode   paged decode attention (one launch)
+  pkv_paged_attention_multi    several new query tokens per sequence, causal
   pkv_reshape_and_cache        write new tokens' K/V into their slots
   pkv_copy_blocks              copy blocks (src -> dst) in both pools: copy-on-write
   pkv_decode_workspace_bytes   workspace size for a decode call
   pkv_decode_num_splits        split count the library will use
+  pkv_multi_workspace_bytes    workspace size for a call with several query tokens
+  pkv_multi_num_splits         its split count
   BlockManager                 the host block manager (pkv_bm_*)
 """
 
@@ -60,6 +63,11 @@ def lib():
         "pkv_paged_attention_decode": (c_int, [c_p, c_int, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_p,
                                                c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_f, c_int,
                                                c_p, c_sz, c_p]),
+        "pkv_multi_workspace_bytes": (c_sz, [c_int] * 8),
+        "pkv_multi_num_splits": (c_int, [c_int] * 8),
+        "pkv_paged_attention_multi": (c_int, [c_p, c_int, c_p, c_int, c_p, c_int, c_int, c_p, c_p, c_int, c_f, c_f,
+                                              c_p, c_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_f,
+                                              c_int, c_p, c_sz, c_p]),
         "pkv_reshape_and_cache": (c_int, [c_p, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_int, c_int, c_int,
                                           c_int, c_int, c_p]),
         "pkv_copy_blocks": (c_int, [c_p, c_p, c_int, c_p, c_int, c_int, c_int, c_int, c_int, c_p]),
@@ -158,6 +166,69 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
     return out
 
 
+def pkv_multi_workspace_bytes(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len,
+                              num_splits=0):
+    return lib().pkv_multi_workspace_bytes(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len,
+                                           max_context_len, num_splits)
+
+
+def pkv_multi_num_splits(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len, num_splits=0):
+    return lib().pkv_multi_num_splits(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len,
+                                      num_splits)
+
+
+def make_multi_workspace(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len, num_splits=0,
+                         device="cuda"):
+    """A zero-filled workspace for pkv_paged_attention_multi (zero once; calls keep it reusable)."""
+    import torch
+    n = pkv_multi_workspace_bytes(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len,
+                                  num_splits)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _multi_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, max_context_len,
+                workspace, scale, k_scale, v_scale, num_splits, stream):
+    import torch
+    T, h_q, D = q.shape
+    NB, h_kv, B, D2 = k_cache.shape
+    S = context_lens.shape[0] if context_lens.dim() == 1 else -1
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (T, h_q, D):
+        raise ValueError("shape mismatch between q / out / k_cache / v_cache")
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must share a dtype")
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"), (query_start, "query_start")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{n} must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(query_start.shape) != (S + 1,):
+        raise ValueError("block_tables must be [S, MB], context_lens [S] and query_start [S + 1]")
+    return (_dev_ptr(out, "out"), dtype_code(out), _dev_ptr(q, "q"), dtype_code(q),
+            _dev_ptr(query_start, "query_start"), T, int(max_query_len),
+            _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), dtype_code(k_cache),
+            float(k_scale), float(v_scale), _dev_ptr(block_tables, "block_tables"),
+            _dev_ptr(context_lens, "context_lens"), S, h_q, h_kv, D, B, NB, block_tables.shape[1],
+            int(max_context_len), float(scale), int(num_splits), _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def pkv_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens, query_start, *, max_query_len,
+                              max_context_len, scale=0.0, k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None,
+                              stream=None):
+    """Causal paged attention of several new query tokens per sequence.
+
+    q, out [T, Hq, D]: rows query_start[s] .. query_start[s+1]-1 are the new
+    tokens of sequence s, at positions ctx_s - m_s + i; context_lens [S]
+    counts them; query_start [S + 1] int32 (all on the GPU).
+    """
+    if workspace is None:
+        S = context_lens.shape[0]
+        workspace = make_multi_workspace(S, q.shape[1], k_cache.shape[1], q.shape[2], k_cache.shape[2],
+                                         max_query_len, max_context_len, num_splits, device=q.device)
+    args = _multi_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len,
+                       max_context_len, workspace, scale, k_scale, v_scale, num_splits, stream)
+    _check(lib().pkv_paged_attention_multi(*args), "pkv_paged_attention_multi")
+    return out
+
+
 class PreparedCall:
     """A C-ABI call whose arguments were validated and marshalled once.
 
@@ -188,6 +259,16 @@ def prepare_paged_attention_decode(out, q, k_cache, v_cache, block_tables, conte
     call = PreparedCall(lib().pkv_paged_attention_decode, args, "pkv_paged_attention_decode",
                         (out, q, k_cache, v_cache, block_tables, context_lens, workspace))
     return call
+
+
+def prepare_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens, query_start, *,
+                                  max_query_len, max_context_len, workspace, scale=0.0, k_scale=1.0, v_scale=1.0,
+                                  num_splits=0, stream=None):
+    """PreparedCall of pkv_paged_attention_multi (same arguments)."""
+    args = _multi_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len,
+                       max_context_len, workspace, scale, k_scale, v_scale, num_splits, stream)
+    return PreparedCall(lib().pkv_paged_attention_multi, args, "pkv_paged_attention_multi",
+                        (out, q, k_cache, v_cache, block_tables, context_lens, query_start, workspace))
 
 
 def prepare_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, *, k_scale=1.0, v_scale=1.0, stream=None):

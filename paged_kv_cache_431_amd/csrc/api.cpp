@@ -57,6 +57,98 @@ bool decode_shape_ok(int num_seqs, int h_q, int h_kv, int head_dim, int block_si
          max_context_len >= 0 && num_splits >= 0;
 }
 
+// Upper bound of max_query_len (keeps every row and grid count within int).
+constexpr int kMaxQueryLen = 1 << 24;
+
+bool multi_shape_ok(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
+                    int max_context_len, int num_splits) {
+  return decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits) &&
+         max_query_len >= 1 && max_query_len <= kMaxQueryLen;
+}
+
+// Splits for several query tokens: the units are (sequence, KV head, row tile).
+int resolve_multi_splits(int num_seqs, int h_q, int h_kv, int max_query_len, int max_context_len, int num_splits) {
+  const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
+  const int64_t units = (int64_t)num_seqs * h_kv * pkv::multi_row_tiles(h_q, h_kv, max_query_len);
+  int n = num_splits > 0 ? num_splits : choose_splits(units, max_tiles);
+  return std::max(1, n);
+}
+
+// Decode (query_start == nullptr: one query token per sequence) and calls
+// with several query tokens per sequence share validation and launch.
+int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
+                  int num_query_tokens, int max_query_len, const void* k_cache, const void* v_cache, int kv_dtype,
+                  float k_scale, float v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                  int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int num_blocks,
+                  int max_blocks_per_seq, int max_context_len, float scale, int num_splits, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  const bool multi = query_start != nullptr;
+  if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return PKV_EINVAL;
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return PKV_EINVAL;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_EINVAL;
+  if (!valid_dtype(out_dtype) || !valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PKV_EINVAL;
+  if (num_seqs == 0 || (multi && num_query_tokens == 0)) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace) return PKV_EINVAL;
+  if (!(std::isfinite(scale))) return PKV_EINVAL;
+  if (kv_dtype == PKV_FP8_E4M3 && !(k_scale > 0.f && std::isfinite(k_scale) && v_scale > 0.f && std::isfinite(v_scale)))
+    return PKV_EINVAL;
+
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if (h_q / h_kv > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
+  if (out_dtype == PKV_FP8_E4M3 || q_dtype == PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
+  const bool pair_ok = (q_dtype == kv_dtype) || (kv_dtype == PKV_FP8_E4M3 && q_dtype != PKV_F32);
+  if (!pair_ok) return PKV_EUNSUPPORTED;
+
+  // matrix-core path: 16-bit or FP8 caches whose blocks hold a power-of-two
+  // number of 16-token tiles; everything else takes the vector path, which
+  // serves one query token per sequence only
+  const int tiles_per_block = block_size / pkv::kTileTokens;
+  const bool matrix_core = kv_dtype != PKV_F32 && block_size % pkv::kTileTokens == 0 &&
+                           (tiles_per_block & (tiles_per_block - 1)) == 0;
+  if (multi && !matrix_core) return PKV_EUNSUPPORTED;
+
+  const int n = multi ? resolve_multi_splits(num_seqs, h_q, h_kv, max_query_len, max_context_len, num_splits)
+                      : resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
+  const int row_tiles = multi ? pkv::multi_row_tiles(h_q, h_kv, max_query_len) : 1;
+  if ((int64_t)ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_tiles * n > INT32_MAX) return PKV_EUNSUPPORTED;
+  const pkv::WorkspaceLayout L = multi ? pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n)
+                                       : pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n);
+  if (workspace_bytes < L.total) return PKV_EWORKSPACE;
+
+  const double s = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)head_dim);
+  const double log2e = 1.4426950408889634;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+
+  pkv::DecodeLaunch a;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_dtype = kv_dtype;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_splits = n;
+  a.tiles_per_split = (int)std::max<int64_t>(1, ceil_div(ceil_div(max_context_len, pkv::kTileTokens), n));
+  a.scale_log2 = (float)(s * log2e * (fp8 ? (double)k_scale : 1.0));
+  a.v_scale = fp8 ? v_scale : 1.f;
+  a.workspace = workspace;
+  a.matrix_core = matrix_core;
+  a.query_start = query_start;
+  a.num_query_tokens = multi ? num_query_tokens : 0;
+  a.max_query_len = multi ? max_query_len : 1;
+  const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,59 +186,39 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, int q_dt
                                int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                                int max_context_len, float scale, int num_splits, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return PKV_EINVAL;
-  if (num_blocks < 1 || max_blocks_per_seq < 1) return PKV_EINVAL;
-  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_EINVAL;
-  if (!valid_dtype(out_dtype) || !valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PKV_EINVAL;
-  if (num_seqs == 0) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace) return PKV_EINVAL;
-  if (!(std::isfinite(scale))) return PKV_EINVAL;
-  if (kv_dtype == PKV_FP8_E4M3 && !(k_scale > 0.f && std::isfinite(k_scale) && v_scale > 0.f && std::isfinite(v_scale)))
+  return run_attention(out, out_dtype, q, q_dtype, nullptr, 0, 1, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                       block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+int pkv_multi_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
+                         int max_context_len, int num_splits) {
+  if (!multi_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len, num_splits)) return 0;
+  return resolve_multi_splits(num_seqs, h_q, h_kv, max_query_len, max_context_len, num_splits);
+}
+
+size_t pkv_multi_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
+                                 int max_context_len, int num_splits) {
+  if (!multi_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len, num_splits)) return 0;
+  const int n = resolve_multi_splits(num_seqs, h_q, h_kv, max_query_len, max_context_len, num_splits);
+  return pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, pkv::multi_row_tiles(h_q, h_kv, max_query_len), n)
+      .total;
+}
+
+int pkv_paged_attention_multi(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
+                              int num_query_tokens, int max_query_len, const void* k_cache, const void* v_cache,
+                              int kv_dtype, float k_scale, float v_scale, const int32_t* block_tables,
+                              const int32_t* context_lens, int num_seqs, int h_q, int h_kv, int head_dim,
+                              int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+                              float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!multi_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len, num_splits))
     return PKV_EINVAL;
-
-  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
-  if (h_q / h_kv > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
-  if (out_dtype == PKV_FP8_E4M3 || q_dtype == PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
-  const bool pair_ok = (q_dtype == kv_dtype) || (kv_dtype == PKV_FP8_E4M3 && q_dtype != PKV_F32);
-  if (!pair_ok) return PKV_EUNSUPPORTED;
-
-  const int n = resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
-  const pkv::WorkspaceLayout L = pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n);
-  if (workspace_bytes < L.total) return PKV_EWORKSPACE;
-
-  const double s = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)head_dim);
-  const double log2e = 1.4426950408889634;
-  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
-
-  pkv::DecodeLaunch a;
-  a.out = out;
-  a.out_dtype = out_dtype;
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.kv_dtype = kv_dtype;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.h_q = h_q;
-  a.h_kv = h_kv;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.num_blocks = num_blocks;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_splits = n;
-  a.tiles_per_split = (int)std::max<int64_t>(1, ceil_div(ceil_div(max_context_len, pkv::kTileTokens), n));
-  a.scale_log2 = (float)(s * log2e * (fp8 ? (double)k_scale : 1.0));
-  a.v_scale = fp8 ? v_scale : 1.f;
-  a.workspace = workspace;
-  // matrix-core path: 16-bit or FP8 caches whose blocks hold a power-of-two
-  // number of 16-token tiles; everything else takes the vector path
-  const int tiles_per_block = block_size / pkv::kTileTokens;
-  a.matrix_core = kv_dtype != PKV_F32 && block_size % pkv::kTileTokens == 0 &&
-                  (tiles_per_block & (tiles_per_block - 1)) == 0;
-  const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+  if (num_query_tokens < 0) return PKV_EINVAL;
+  if (num_seqs > 0 && !query_start) return PKV_EINVAL;
+  return run_attention(out, out_dtype, q, q_dtype, query_start, num_query_tokens, max_query_len, k_cache, v_cache,
+                       kv_dtype, k_scale, v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, num_splits, workspace,
+                       workspace_bytes, stream);
 }
 
 int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype, void* k_cache, void* v_cache,

@@ -93,28 +93,61 @@ struct Params {
   int tile_shift;  // log2(block_size / 16) on the matrix-core path
   float scale_log2, v_scale;
   int out_dtype;
+  // Several query tokens per sequence (null for decode): the query rows of
+  // sequence s are [query_start[s], query_start[s + 1]) of q and out.
+  const int32_t* query_start;
+  int num_query_tokens, max_query_len;
+  int row_tiles;  // 16-row tiles of (query token, head) rows per (sequence, KV head)
 };
 
 struct Item {
   int s, kvh, unit, split, ctx, n_tiles, n_splits_seq, t_begin, t_end;
+  int rt, m, q0;  // several query tokens: row tile, query tokens of the sequence, first query row
 };
 
 // Workgroup id -> work item.  Consecutive workgroup ids go to the 8 XCDs in
 // turn, so every split of one (sequence, KV head) gets an id with the same
-// residue mod 8: their partial results meet in one XCD's L2.
+// residue mod 8: their partial results meet in one XCD's L2.  With several
+// query tokens (MT) the row tiles of one (sequence, KV head) share that
+// residue too, so they read its K/V through the same L2.
+//
+// Query token i of the m new tokens of a sequence with ctx cached tokens
+// (its own K/V included) sits at position ctx - m + i and attends to the
+// positions up to and including its own.
+template <bool MT>
 __device__ __forceinline__ bool get_item(const Params& p, Item& it) {
   const int wg = blockIdx.x;
   const int j = wg >> 3;
   it.unit = (j / p.num_splits) * 8 + (wg & 7);
   it.split = j % p.num_splits;
-  if (it.unit >= p.units) return false;
-  it.s = it.unit / p.h_kv;
-  it.kvh = it.unit - it.s * p.h_kv;
+  int base = it.unit;  // (sequence, KV head) index
+  it.rt = 0;
+  if constexpr (MT) {
+    const int y = it.unit >> 3;
+    it.rt = y % p.row_tiles;
+    base = (y / p.row_tiles) * 8 + (it.unit & 7);
+  }
+  if (base >= p.units) return false;
+  it.s = base / p.h_kv;
+  it.kvh = base - it.s * p.h_kv;
   int ctx = p.context_lens[it.s];
   const int cap = p.max_blocks_per_seq * p.block_size;
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   it.ctx = ctx;
-  it.n_tiles = (ctx + kTileTokens - 1) / kTileTokens;
+  int n_tok = ctx;  // positions any row of the item attends to: [0, n_tok)
+  if constexpr (MT) {
+    // rows beyond the query table are clamped away, never read or written
+    int q0 = p.query_start[it.s], q1 = p.query_start[it.s + 1];
+    q0 = min(max(q0, 0), p.num_query_tokens);
+    q1 = min(max(q1, q0), p.num_query_tokens);
+    it.q0 = q0;
+    it.m = min(q1 - q0, p.max_query_len);
+    const int first_row = it.rt * 16;
+    if (first_row >= it.m * p.group) return false;  // no query row in this tile
+    const int i_last = min(it.m - 1, (first_row + 15) / p.group);
+    n_tok = min(ctx, max(0, ctx - it.m + i_last + 1));
+  }
+  it.n_tiles = (n_tok + kTileTokens - 1) / kTileTokens;
   int ns = (it.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   it.n_splits_seq = ns > p.num_splits ? p.num_splits : ns;
   const int per = it.n_splits_seq > 0 ? (it.n_tiles + it.n_splits_seq - 1) / it.n_splits_seq : 0;
@@ -182,32 +215,52 @@ __device__ __forceinline__ void store_out(const Params& p, size_t row, int chunk
   }
 }
 
-// Sequences with an empty context attend over nothing: their output is 0.
-template <int D>
+// Output row of row r (0..15) of an item, false if the row holds no query:
+// decode rows are the group's query heads; with several query tokens row
+// r is (query token, head) = divmod(16 * rt + r, group).
+template <bool MT>
+__device__ __forceinline__ bool out_row(const Params& p, const Item& it, int r, size_t& row) {
+  const int G = p.group;
+  if constexpr (MT) {
+    const int gr = it.rt * 16 + r;
+    const int i = gr / G;
+    row = (size_t)(it.q0 + i) * p.h_q + it.kvh * G + (gr - i * G);
+    return i < it.m;
+  } else {
+    row = (size_t)it.s * p.h_q + it.kvh * G + r;
+    return r < G;
+  }
+}
+
+// Rows that attend over nothing (an empty context) get 0.
+template <int D, bool MT>
 __device__ void write_zeros(const Params& p, const Item& it) {
   constexpr int DW = D / 16;
   const int g = threadIdx.x >> 4, chunk = threadIdx.x & 15;
-  if (g >= p.group) return;
+  size_t row;
+  if (!out_row<MT>(p, it, g, row)) return;
   float z[DW];
 #pragma unroll
   for (int e = 0; e < DW; ++e) z[e] = 0.f;
-  store_out<D>(p, (size_t)it.s * p.h_q + it.kvh * p.group + g, chunk, z, 1.f);
+  store_out<D>(p, row, chunk, z, 1.f);
 }
 
 // Merge the 4 waves' states (already in `sm`, after a barrier), then either
 // write the output (one range) or publish this range's partial state and let
 // the last range of the (sequence, KV head) combine all of them.
-template <int D>
+template <int D, bool MT>
 __device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
   constexpr int DW = D / 16;
   const int t = threadIdx.x;
   const int g = t >> 4, chunk = t & 15;
-  const int G = p.group;
+  const int R = MT ? 16 : p.group;  // rows of an item (partial-state rows per split)
+  size_t row;
+  const bool row_ok = out_row<MT>(p, it, g, row);
   float a[DW];
   float mstar = kNegInf, lstar = 0.f;
 #pragma unroll
   for (int e = 0; e < DW; ++e) a[e] = 0.f;
-  if (g < G) {
+  if (row_ok) {
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) mstar = fmaxf(mstar, sm.m[w][g]);
 #pragma unroll
@@ -218,14 +271,15 @@ __device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
       for (int e = 0; e < DW; ++e) a[e] += f * sm.acc[w][g][chunk * DW + e];
     }
   }
-  const size_t row = (size_t)it.s * p.h_q + it.kvh * G + g;
+  // a row that sees no position (only with several query tokens, when a
+  // sequence has more new tokens than cached ones) gets 0
   if (it.n_splits_seq == 1) {
-    if (g < G) store_out<D>(p, row, chunk, a, p.v_scale / lstar);
+    if (row_ok) store_out<D>(p, row, chunk, a, lstar > 0.f ? p.v_scale / lstar : 0.f);
     return;
   }
-  const size_t base = (size_t)it.unit * p.num_splits * G + g;  // partial row of split 0
-  if (g < G) {
-    const size_t prow = base + (size_t)it.split * G;
+  const size_t base = (size_t)it.unit * p.num_splits * R + g;  // partial row of split 0
+  if (row_ok) {
+    const size_t prow = base + (size_t)it.split * R;
     float* dst = p.ws_acc + prow * D + chunk * DW;
 #pragma unroll
     for (int e = 0; e < DW; ++e) store_agent(dst + e, a[e]);
@@ -244,15 +298,15 @@ __device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
   }
   __syncthreads();
   if (!sm.flag) return;
-  if (g >= G) return;
+  if (!row_ok) return;
   float mm = kNegInf;
-  for (int sp = 0; sp < it.n_splits_seq; ++sp) mm = fmaxf(mm, load_agent(p.ws_ml + 2 * (base + (size_t)sp * G)));
+  for (int sp = 0; sp < it.n_splits_seq; ++sp) mm = fmaxf(mm, load_agent(p.ws_ml + 2 * (base + (size_t)sp * R)));
   float ll = 0.f;
   float o[DW];
 #pragma unroll
   for (int e = 0; e < DW; ++e) o[e] = 0.f;
   for (int sp = 0; sp < it.n_splits_seq; ++sp) {
-    const size_t prow = base + (size_t)sp * G;
+    const size_t prow = base + (size_t)sp * R;
     const float m_i = load_agent(p.ws_ml + 2 * prow);
     const float l_i = load_agent(p.ws_ml + 2 * prow + 1);
     const float f = mm == kNegInf ? 0.f : fast_exp2(m_i - mm);
@@ -261,7 +315,7 @@ __device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
 #pragma unroll
     for (int e = 0; e < DW; ++e) o[e] += f * load_agent(src + e);
   }
-  store_out<D>(p, row, chunk, o, p.v_scale / ll);
+  store_out<D>(p, row, chunk, o, ll > 0.f ? p.v_scale / ll : 0.f);
 }
 
 // ---------------------------------------------------------------- matrix-core path
@@ -335,10 +389,11 @@ struct MfmaTile {
   static constexpr int NBUF = TILE_BYTES >= 8192 ? 2 : 3;
   u32x4 k[KCH];
   uint32_t v[4][VDW];
-  int lim;  // valid tokens in the tile (0..16)
+  int lim;   // valid tokens in the tile (0..16)
+  int tok0;  // position of its first token
 };
 
-template <int KV, int CT, int D>
+template <int KV, int CT, int D, bool MT>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd))) void decode_mfma_kernel(
     Params p) {
   using Tile = MfmaTile<KV, D>;
@@ -358,9 +413,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   } sm;
 
   Item it;
-  if (!get_item(p, it)) return;
+  if (!get_item<MT>(p, it)) return;
   if (it.n_tiles == 0) {
-    if (it.split == 0) write_zeros<D>(p, it);
+    if (it.split == 0) write_zeros<D, MT>(p, it);
     return;
   }
   if (it.split >= it.n_splits_seq) return;
@@ -373,15 +428,31 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int q4 = lane >> 4;
   const int G = p.group;
 
-  // Q as the B operand: column g = lo16, same d order as the K chunks.
+  // Q as the B operand: column lo16 is row lo16 of the item (a query head;
+  // with several query tokens a (query token, head) pair), same d order as
+  // the K chunks.  Padding rows hold zeros and never form an address outside
+  // the item's rows.  row_lim: positions [0, row_lim) this row attends to.
   u32x4 qop[NK];
+  int row_lim = it.ctx;
   {
-    const int g_load = lo16 < G ? lo16 : G - 1;  // padding rows never form an address past the group
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)it.s * p.h_q + it.kvh * G + g_load) * D;
+    bool row_ok;
+    size_t qr;
+    if constexpr (MT) {
+      const int gr = it.rt * 16 + lo16;
+      const int i = gr / G;
+      row_ok = i < it.m;
+      const int ic = row_ok ? i : it.m - 1;  // it.m >= 1 for an item with rows
+      qr = (size_t)(it.q0 + ic) * p.h_q + it.kvh * G + (row_ok ? gr - i * G : 0);
+      row_lim = min(it.ctx, max(0, it.ctx - it.m + ic + 1));
+    } else {
+      row_ok = lo16 < G;
+      qr = (size_t)it.s * p.h_q + it.kvh * G + (row_ok ? lo16 : G - 1);
+    }
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int d0 = KV == kFP8 ? 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1) : 32 * kk + 8 * q4;
-      qop[kk] = lo16 < G ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
+      qop[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -462,10 +533,12 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
 
     // 3) online softmax (log2 domain); row g = lo16, tokens 4*q4 + rr
     float s[4];
+    // causal limit of this lane's row within the tile (several query tokens)
+    const int row_cut = MT ? min(lim, row_lim - r.tok0) : lim;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       s[rr] = sc[rr] * p.scale_log2;
-      if (partial && 4 * q4 + rr >= lim) s[rr] = kNegInf;
+      if ((MT || partial) && 4 * q4 + rr >= row_cut) s[rr] = kNegInf;
     }
     // Each lane tests its own 4 scores against its row's running max.  Only
     // when a lane of the wave exceeds it by more than the slack (always for
@@ -553,6 +626,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       phys = ok ? phys : 0;
       const int rem = it.ctx - tok0;
       r.lim = ok ? (rem < kTileTokens ? rem : kTileTokens) : 0;
+      r.tok0 = tok0;
       const int sub = (t0 + j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
       const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
       const uint8_t* kp = kbase + off;
@@ -606,7 +680,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     sm.merge.l[wave][lo16] = l_row;
   }
   __syncthreads();
-  finish<D>(p, it, sm.merge);
+  finish<D, MT>(p, it, sm.merge);
 }
 
 // ---------------------------------------------------------------- vector path
@@ -630,9 +704,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_vector_kernel(Params p)
   __shared__ MergeSmem<D> sm;
 
   Item it;
-  if (!get_item(p, it)) return;
+  if (!get_item<false>(p, it)) return;
   if (it.n_tiles == 0) {
-    if (it.split == 0) write_zeros<D>(p, it);
+    if (it.split == 0) write_zeros<D, false>(p, it);
     return;
   }
   if (it.split >= it.n_splits_seq) return;
@@ -701,7 +775,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_vector_kernel(Params p)
     }
   }
   __syncthreads();
-  finish<D>(p, it, sm);
+  finish<D, false>(p, it, sm);
 }
 
 template <typename K>
@@ -710,13 +784,23 @@ hipError_t launch(K kernel, int grid, const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool MT>
+hipError_t dispatch_mfma(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
+  if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kBF16, kBF16, D, MT>, grid, p, s);
+  if (a.kv_dtype == kF16 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kF16, kF16, D, MT>, grid, p, s);
+  if (a.kv_dtype == kFP8 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kFP8, kBF16, D, MT>, grid, p, s);
+  if (a.kv_dtype == kFP8 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kFP8, kF16, D, MT>, grid, p, s);
+  return hipErrorInvalidValue;
+}
+
 template <int D>
 hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
+  if (a.query_start != nullptr) {
+    if (!a.matrix_core) return hipErrorInvalidValue;
+    return dispatch_mfma<D, true>(a, grid, p, s);
+  }
   if (a.matrix_core) {
-    if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kBF16, kBF16, D>, grid, p, s);
-    if (a.kv_dtype == kF16 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kF16, kF16, D>, grid, p, s);
-    if (a.kv_dtype == kFP8 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kFP8, kBF16, D>, grid, p, s);
-    if (a.kv_dtype == kFP8 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kFP8, kF16, D>, grid, p, s);
+    return dispatch_mfma<D, false>(a, grid, p, s);
   } else {
     if (a.kv_dtype == kF32 && a.q_dtype == kF32) return launch(decode_vector_kernel<kF32, kF32, D>, grid, p, s);
     if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_vector_kernel<kBF16, kBF16, D>, grid, p, s);
@@ -741,8 +825,23 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int hea
   return L;
 }
 
+WorkspaceLayout multi_workspace_layout(int num_seqs, int h_kv, int head_dim, int row_tiles, int num_splits) {
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t units = (((size_t)num_seqs * h_kv + 7) / 8) * 8 * row_tiles;
+  const size_t rows = units * num_splits * 16;
+  WorkspaceLayout L;
+  L.counters = 0;
+  L.ml = align(units * sizeof(int32_t));
+  L.acc = L.ml + align(rows * 2 * sizeof(float));
+  L.total = L.acc + align(rows * head_dim * sizeof(float));
+  return L;
+}
+
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
-  const WorkspaceLayout L = decode_workspace_layout(a.num_seqs, a.h_q, a.h_kv, a.head_dim, a.num_splits);
+  const bool multi = a.query_start != nullptr;
+  const int row_tiles = multi ? multi_row_tiles(a.h_q, a.h_kv, a.max_query_len) : 1;
+  const WorkspaceLayout L = multi ? multi_workspace_layout(a.num_seqs, a.h_kv, a.head_dim, row_tiles, a.num_splits)
+                                  : decode_workspace_layout(a.num_seqs, a.h_q, a.h_kv, a.head_dim, a.num_splits);
   Params p;
   p.out = a.out;
   p.q = a.q;
@@ -768,7 +867,11 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.scale_log2 = a.scale_log2;
   p.v_scale = a.v_scale;
   p.out_dtype = a.out_dtype;
-  const int grid = ((p.units + 7) / 8) * 8 * a.num_splits;
+  p.query_start = a.query_start;
+  p.num_query_tokens = a.num_query_tokens;
+  p.max_query_len = a.max_query_len;
+  p.row_tiles = row_tiles;
+  const int grid = ((p.units + 7) / 8) * 8 * row_tiles * a.num_splits;
   if (grid == 0) return hipSuccess;
   if (a.head_dim == 128) return dispatch<128>(a, grid, p, stream);
   if (a.head_dim == 64) return dispatch<64>(a, grid, p, stream);

@@ -35,7 +35,17 @@ struct DecodeLaunch {
   float v_scale;        // output scale (FP8 V), else 1
   void* workspace;
   bool matrix_core;     // MFMA path (else the vector path)
+  // Several query tokens per sequence (query_start != nullptr; matrix-core
+  // path only): q and out are [num_query_tokens, h_q, head_dim], the rows of
+  // sequence s are [query_start[s], query_start[s + 1]), at most max_query_len.
+  const int32_t* query_start;
+  int num_query_tokens, max_query_len;
 };
+
+// 16-row tiles of (query token, query head) rows per (sequence, KV head).
+inline int multi_row_tiles(int h_q, int h_kv, int max_query_len) {
+  return (int)(((int64_t)max_query_len * (h_q / h_kv) + 15) / 16);
+}
 
 // Byte layout of the decode workspace.
 struct WorkspaceLayout {
@@ -46,6 +56,11 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits);
+
+// Workspace of a call with several query tokens per sequence: one counter
+// and 16 partial-state rows per split for each (sequence, KV head, row tile),
+// (sequence, KV head) pairs counted in whole groups of 8.
+WorkspaceLayout multi_workspace_layout(int num_seqs, int h_kv, int head_dim, int row_tiles, int num_splits);
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 

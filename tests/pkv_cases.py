@@ -71,6 +71,18 @@ class Case:
             num_splits=num_splits, workspace=workspace)
         return out
 
+    def multi(self, q, query_start, max_query_len, out_dtype=torch.float32, num_splits=0, out=None, workspace=None):
+        """Several new query tokens per sequence (q [T, Hq, D]) over the pools."""
+        wl = self.wl
+        if out is None:
+            out = torch.empty((q.shape[0], wl.h_q, wl.head_dim), dtype=out_dtype, device=self.device)
+        qs = torch.from_numpy(np.asarray(query_start, dtype=np.int32)).to(self.device)
+        pkv.pkv_paged_attention_multi(
+            out, q, self.t.k_cache, self.t.v_cache, self.block_tables, self.context_lens, qs,
+            max_query_len=max_query_len, max_context_len=self.plan.max_context_len, k_scale=self.t.k_scale,
+            v_scale=self.t.v_scale, num_splits=num_splits, workspace=workspace)
+        return out
+
     # ---------------------------------------------------------------- oracle
     def oracle_pools(self):
         """Pools after the oracle's scatter of the new tokens (host arrays)."""
@@ -89,6 +101,14 @@ class Case:
             to_bits(self.t.q), kc, vc, self.rp.block_tables, self.plan.context_lens, q_dtype=wl.q_dtype,
             kv_dtype=wl.kv_dtype, block_size=wl.block_size, scale=1.0 / math.sqrt(wl.head_dim),
             k_scale=self.t.k_scale, v_scale=self.t.v_scale, seqs=seqs)
+
+    def oracle_multi(self, q, query_start, seqs=None):
+        wl = self.wl
+        kc, vc = self.oracle_pools()
+        return oracle.attention.paged_attention_multi(
+            to_bits(q), kc, vc, self.rp.block_tables, self.plan.context_lens, np.asarray(query_start),
+            q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype, block_size=wl.block_size,
+            scale=1.0 / math.sqrt(wl.head_dim), k_scale=self.t.k_scale, v_scale=self.t.v_scale, seqs=seqs)
 
 
 def errors(got, ref, seqs=None):

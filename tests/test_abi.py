@@ -88,6 +88,49 @@ def test_decode_rejects_bad_scalars_without_launching(over, status):
     assert _decode(**over) == status
 
 
+def _multi(**over):
+    args = dict(out=1, out_dtype=0, q=1, q_dtype=2, qs=1, T=12, mql=4, k=1, v=1, kv=2, ks=1.0, vs=1.0, bt=1, cl=1,
+                S=4, hq=8, hkv=2, d=128, bs=16, nb=10, mb=4, maxctx=64, scale=0.0, splits=0, ws=1, wsb=1 << 30,
+                stream=None)
+    args.update(over)
+    a = args
+    P = ctypes.c_void_p
+    return pkv.lib().pkv_paged_attention_multi(
+        P(a["out"]), a["out_dtype"], P(a["q"]), a["q_dtype"], P(a["qs"]), a["T"], a["mql"], P(a["k"]), P(a["v"]),
+        a["kv"], a["ks"], a["vs"], P(a["bt"]), P(a["cl"]), a["S"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
+        a["mb"], a["maxctx"], a["scale"], a["splits"], P(a["ws"]), a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(qs=None), pkv.PKV_EINVAL),                # no query table
+    (dict(T=-1), pkv.PKV_EINVAL),
+    (dict(mql=0), pkv.PKV_EINVAL),
+    (dict(mql=(1 << 24) + 1), pkv.PKV_EINVAL),
+    (dict(hq=6, hkv=4), pkv.PKV_EINVAL),
+    (dict(maxctx=65), pkv.PKV_EINVAL),
+    (dict(kv=0, q_dtype=0), pkv.PKV_EUNSUPPORTED),  # fp32 caches: vector path, one query token only
+    (dict(bs=8, mb=8), pkv.PKV_EUNSUPPORTED),       # blocks that are not whole 16-token tiles
+    (dict(bs=48, mb=2), pkv.PKV_EUNSUPPORTED),      # three tiles per block
+    (dict(d=96), pkv.PKV_EUNSUPPORTED),
+    (dict(wsb=16), pkv.PKV_EWORKSPACE),
+    (dict(T=0), pkv.PKV_OK),                        # no query rows: nothing launched
+    (dict(S=0, qs=None), pkv.PKV_OK),
+])
+def test_multi_rejects_bad_scalars_without_launching(over, status):
+    assert _multi(**over) == status
+
+
+def test_multi_workspace_and_split_sizing():
+    # 47 sequences, 4 new tokens each, 64 query heads on 8 KV heads: 2 row tiles
+    n = pkv.pkv_multi_num_splits(47, 64, 8, 128, 16, 4, 829)
+    assert n >= 1
+    units = 47 * 8 * 2                               # (sequence, KV head) pairs (376 = 47 groups of 8) x row tiles
+    assert pkv.pkv_multi_workspace_bytes(47, 64, 8, 128, 16, 4, 829, 3) >= units * 3 * 16 * (128 + 2) * 4
+    assert pkv.pkv_multi_num_splits(47, 64, 8, 128, 16, 4, 829, 3) == 3
+    assert pkv.pkv_multi_workspace_bytes(47, 64, 8, 128, 16, 0, 829) == 0
+    assert pkv.pkv_multi_num_splits(4, 6, 4, 64, 16, 2, 100) == 0
+
+
 def test_reshape_and_cache_rejects_bad_scalars():
     L = pkv.lib()
     P = ctypes.c_void_p
