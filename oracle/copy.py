@@ -1,4 +1,6 @@
-"""copy_blocks: the block copy that completes copy-on-write.
+"""copy_blocks: the block copy that completes copy-on-write; swap_blocks: the
+block move between a device pool and a host pool that preemption by swapping
+makes.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -36,4 +38,41 @@ def copy_blocks(k_cache, v_cache, pairs):
     for src, dst in zip(srcs, dsts):
         k_out[dst] = k_cache[src]
         v_out[dst] = v_cache[src]
+    return k_out, v_out
+
+
+# ---------------------------------------------------------------- swapping
+#
+# When the device pool fills, a running sequence can be preempted by moving
+# its KV blocks to host memory and paging them back later instead of
+# recomputing them ([AF] "Beyond paging: radix trees and continuous
+# batching"; [OT] "Offload").  The move itself is a block copy between two
+# different pools; the sequence comes back into whatever device blocks the
+# allocator hands out then, with a new block table.
+#
+# Readings: block s of the source pools goes to block d of the destination
+# pools, every KV head and slot, K and V; a destination may not repeat and
+# every id must lie inside its pool (those calls are rejected).
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs):
+    """Return (dst_k, dst_v) copies with block d := block s of (src_k, src_v)
+    for every (s, d) row of pairs ([n, 2] int)."""
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("pools disagree in [h_kv, block_size, head_dim]")
+    srcs, dsts = pairs[:, 0].tolist(), pairs[:, 1].tolist()
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("a destination block repeats")
+    for b in srcs:
+        if not 0 <= b < src_k.shape[0]:
+            raise ValueError(f"source block {b} outside a pool of {src_k.shape[0]} blocks")
+    for b in dsts:
+        if not 0 <= b < dst_k.shape[0]:
+            raise ValueError(f"destination block {b} outside a pool of {dst_k.shape[0]} blocks")
+    k_out = np.array(dst_k, copy=True)
+    v_out = np.array(dst_v, copy=True)
+    for s, d in zip(srcs, dsts):
+        k_out[d] = src_k[s]
+        v_out[d] = src_v[s]
     return k_out, v_out
