@@ -14,6 +14,8 @@ launch duration (HIP events on its stream around back-to-back launches over
 the layer pools); traffic = HBM bytes per launch from rocprofv3 counters,
 reported only while the kernel source is the one they were taken on.
 copy_blocks = the block copy of copy-on-write (1,024 block pairs, K and V).
+swap_blocks = preemption by swap: 1,024 scattered blocks (K and V) to pinned
+host memory and back in one launch each way, GB/s against PCIe 5.0 x16.
 multi_query = a speculative step: 4 new query tokens per sequence (the last 4
 positions of each context, causal), the same pools; GB/s counts each cached
 K/V byte once.
@@ -42,12 +44,16 @@ DEFAULT_WORKLOAD = "gqa70b-bf16-47x825"
 # WRITE_SIZE: on a 1 GiB device copy FETCH_SIZE reads half the bytes read and
 # WRITE_SIZE all the bytes written), valid only for the kernel source they
 # were taken on (its SHA-256) and the workload / split count they ran.
+# Host link of an MI355X: PCIe 5.0 x16, per direction.
+PCIE_PEAK_GBS = 64.0
+
 # Lookahead tokens per sequence of the speculative step measured beside decode.
 MULTI_TOKENS = 4
 
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("00e218a4533513a0179d5e27618465151b12c228accc59e868b79ba58856d21d", "gqa70b-bf16-47x825", 1): 162715853,
+    ("ab32f66652a4ae393ae288e82ccd4a34bc14b34f2d42818a1a1ffb1af737e1d1", "gqa70b-bf16-47x825", 1): 162697421,
+    ("ab32f66652a4ae393ae288e82ccd4a34bc14b34f2d42818a1a1ffb1af737e1d1", "gqa70b-bf16-47x825-multi4", 1): 171542733,
 }
 
 
@@ -119,6 +125,49 @@ def cpu_baseline(plan, rp, tensors, budget_s):
             "seqs_per_s": round(done_seqs / dt, 3), "host_cpus": os.cpu_count(),
             "sample": f"{done_calls} repeats of one layer call of {wl.name} ({wl.num_seqs} sequences: scatter of the "
                       f"new tokens, then float64 attention one sequence at a time), {dt:.1f} s"}
+
+
+def swap_measurement(pkv, t, plan, wl, stream, n_pairs, _hbm_peak):
+    """Preemption by swap: n_pairs scattered blocks (K and V) of one layer pool
+    to a pinned host pool and back, one launch each way; the latency of a
+    one-block swap; and, for reference, the DMA engines' rate for one
+    contiguous pinned buffer of the same size."""
+    import numpy as np
+    import torch
+    block_bytes = wl.h_kv * wl.block_size * wl.head_dim * t.k_cache.element_size()
+    shape = (n_pairs,) + tuple(t.k_cache.shape[1:])
+    hk = torch.empty(shape, dtype=t.k_cache.dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=t.v_cache.dtype, pin_memory=True)
+    dev_blocks = np.random.default_rng(11).permutation(plan.num_blocks)[:n_pairs]
+    out_pairs = torch.from_numpy(np.stack([dev_blocks, np.arange(n_pairs)], axis=1).astype(np.int32)).cuda()
+    in_pairs = torch.from_numpy(np.stack([np.arange(n_pairs), dev_blocks], axis=1).astype(np.int32)).cuda()
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]  # median, ms
+
+    moved = n_pairs * 2 * block_bytes
+    d2h = timed(lambda: pkv.pkv_swap_blocks(hk, hv, t.k_cache, t.v_cache, out_pairs, stream=stream), 10)
+    h2d = timed(lambda: pkv.pkv_swap_blocks(t.k_cache, t.v_cache, hk, hv, in_pairs, stream=stream), 10)
+    one_d2h = timed(lambda: pkv.pkv_swap_blocks(hk, hv, t.k_cache, t.v_cache, out_pairs[:1], stream=stream), 20)
+    one_h2d = timed(lambda: pkv.pkv_swap_blocks(t.k_cache, t.v_cache, hk, hv, in_pairs[:1], stream=stream), 20)
+    flat_h = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+    flat_d = torch.empty(moved, dtype=torch.uint8, device="cuda")
+    dma_d2h = timed(lambda: flat_h.copy_(flat_d, non_blocking=True), 10)
+    dma_h2d = timed(lambda: flat_d.copy_(flat_h, non_blocking=True), 10)
+    gbps = lambda ms: round(moved / (ms * 1e-3) / 1e9, 2)
+    return {"pairs": n_pairs, "bytes_per_call": moved, "peak_GBps": PCIE_PEAK_GBS,
+            "d2h_us": round(d2h * 1e3, 2), "d2h_GBps": gbps(d2h), "d2h_frac": round(gbps(d2h) / PCIE_PEAK_GBS, 4),
+            "h2d_us": round(h2d * 1e3, 2), "h2d_GBps": gbps(h2d), "h2d_frac": round(gbps(h2d) / PCIE_PEAK_GBS, 4),
+            "one_block_d2h_us": round(one_d2h * 1e3, 2), "one_block_h2d_us": round(one_h2d * 1e3, 2),
+            "dma_contiguous_d2h_GBps": gbps(dma_d2h), "dma_contiguous_h2d_GBps": gbps(dma_h2d)}
 
 
 def main():
@@ -307,8 +356,11 @@ def main():
         "num_splits": pkv.pkv_multi_num_splits(wl.num_seqs, wl.h_q, wl.h_kv, wl.head_dim, wl.block_size, m,
                                                plan.max_context_len, 0),
         "mean_launch_us": round(multi_ms * 1e3, 3),
+        "traffic": measured_traffic(f"{wl.name}-multi{m}", pkv.pkv_multi_num_splits(
+            wl.num_seqs, wl.h_q, wl.h_kv, wl.head_dim, wl.block_size, m, plan.max_context_len, 0)),
         "kv_GBps": round(per_call / (multi_ms * 1e-3) / 1e9, 2),
         "frac_of_hbm_peak": round(per_call / (multi_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    result["swap_blocks"] = swap_measurement(pkv, pools[0], plan, wl, stream, n_pairs, HBM_PEAK_GBS)
     if not args.no_cpu_baseline:
         del pools, decodes, scatters, layer_calls, multis
         torch.cuda.empty_cache()

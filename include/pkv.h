@@ -230,6 +230,35 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, const int32_t* b
                     int h_kv, int head_dim, int block_size, int num_blocks, void* stream);
 
 /* ------------------------------------------------------------------------
+ * swap_blocks: move whole blocks between two pools, typically a device pool
+ * and a pool in pinned host memory.
+ *
+ * When the device pool fills, a sequence can be preempted by moving its KV
+ * blocks to host memory over PCIe and paging them back later instead of
+ * recomputing them ("KV cache and PagedAttention in serving", section
+ * "Beyond paging: radix trees and continuous batching"); every such transfer
+ * costs interconnect bandwidth and time ("Paged KV Cache" tutorial, section
+ * "Offload").  One call moves any number of scattered blocks in one launch:
+ * block src of the source pools goes to block dst of the destination pools,
+ * every KV head and slot, K and V.
+ *   dst_k, dst_v  [dst_num_blocks, Hkv, B, D] in kv_dtype
+ *   src_k, src_v  [src_num_blocks, Hkv, B, D] in kv_dtype
+ *   block_pairs   [num_pairs, 2] int32: (src block, dst block) per row; a
+ *                 row with an id outside its pool is skipped; a destination
+ *                 must not repeat, and the two pools must not overlap
+ *                 (caller errors, not checked).
+ * Every pointer must be memory of the current device or pinned host memory
+ * (hipHostMalloc, or a tensor allocated pinned); pageable memory and other
+ * devices' memory return PKV_EINVAL before anything is launched.  The copy
+ * is ordered on `stream`; host memory it writes is complete once the stream
+ * has been synchronised.  h_kv * B * D * element bytes must be a multiple of
+ * 16.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
+ * ------------------------------------------------------------------------ */
+int pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* src_k, const void* src_v,
+                    int src_num_blocks, int kv_dtype, const int32_t* block_pairs, int num_pairs, int h_kv,
+                    int head_dim, int block_size, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block manager (no device memory; pure host bookkeeping)
  *
  * Blocks are handed out only as a sequence grows ("AI Engineering

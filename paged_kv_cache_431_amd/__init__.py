@@ -13,6 +13,7 @@ HIP stream to the C ABI declared in include/pkv.h (same function names).
   pkv_paged_attention_multi    several new query tokens per sequence, causal
   pkv_reshape_and_cache        write new tokens' K/V into their slots
   pkv_copy_blocks              copy blocks (src -> dst) in both pools: copy-on-write
+  pkv_swap_blocks              move blocks between a device pool and a pinned host pool
   pkv_decode_workspace_bytes   workspace size for a decode call
   pkv_decode_num_splits        split count the library will use
   pkv_multi_workspace_bytes    workspace size for a call with several query tokens
@@ -71,6 +72,7 @@ def lib():
         "pkv_reshape_and_cache": (c_int, [c_p, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_int, c_int, c_int,
                                           c_int, c_int, c_p]),
         "pkv_copy_blocks": (c_int, [c_p, c_p, c_int, c_p, c_int, c_int, c_int, c_int, c_int, c_p]),
+        "pkv_swap_blocks": (c_int, [c_p, c_p, c_int, c_p, c_p, c_int, c_int, c_p, c_int, c_int, c_int, c_int, c_p]),
         "pkv_bm_create": (c_int, [c_i32, c_i32, p_i32, ctypes.POINTER(c_p)]),
         "pkv_bm_destroy": (None, [c_p]),
         "pkv_bm_append": (c_int, [c_p, c_i32, c_i32, p_i64, p_i32, p_i32]),
@@ -311,6 +313,35 @@ def pkv_copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
                                _dev_ptr(block_pairs, "block_pairs"), block_pairs.shape[0], h_kv, D, B, NB,
                                _stream(stream))
     _check(st, "pkv_copy_blocks")
+
+
+def _pool_ptr(t, name):
+    """Device pointer of a GPU tensor or address of a pinned host tensor."""
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a GPU tensor or a pinned host tensor (pin_memory=True)")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pkv_swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, *, stream=None):
+    """Copy block src of (src_k, src_v) to block dst of (dst_k, dst_v) for each
+    row (src, dst) of block_pairs [n, 2] int32, in one launch.  Pools are
+    [NB, Hkv, B, D] on the GPU or in pinned host memory (swap out: device ->
+    host, swap in: host -> device); block_pairs on the GPU or pinned."""
+    import torch
+    if src_k.dtype != dst_k.dtype or src_v.dtype != src_k.dtype or dst_v.dtype != dst_k.dtype:
+        raise ValueError("all four pools must share a dtype")
+    if tuple(src_k.shape[1:]) != tuple(dst_k.shape[1:]) or src_v.shape != src_k.shape or dst_v.shape != dst_k.shape:
+        raise ValueError("pools must agree in [Hkv, B, D], and K with V")
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2] int32")
+    _, h_kv, B, D = src_k.shape
+    st = lib().pkv_swap_blocks(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), dst_k.shape[0],
+                               _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"), src_k.shape[0],
+                               dtype_code(src_k), _pool_ptr(block_pairs, "block_pairs"), block_pairs.shape[0],
+                               h_kv, D, B, _stream(stream))
+    _check(st, "pkv_swap_blocks")
 
 
 class BlockManager:

@@ -57,6 +57,31 @@ bool decode_shape_ok(int num_seqs, int h_q, int h_kv, int head_dim, int block_si
          max_context_len >= 0 && num_splits >= 0;
 }
 
+// The address a kernel on the current device uses for p: p itself for memory
+// of that device, the mapped address for pinned host memory; false for
+// pageable host memory, other devices' memory, or anything unknown.
+bool device_address(const void* p, void** out) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // keep the failed query from surfacing at the next launch
+    return false;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (a.type == hipMemoryTypeDevice && a.device == dev && a.devicePointer != nullptr) {
+    *out = const_cast<void*>(p);
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer != nullptr) {
+    // the mapped address of p itself, whether the runtime reports the two
+    // addresses at p or at the start of the allocation
+    const char* host = a.hostPointer ? static_cast<const char*>(a.hostPointer) : static_cast<const char*>(p);
+    *out = static_cast<char*>(a.devicePointer) + (static_cast<const char*>(p) - host);
+    return true;
+  }
+  return false;
+}
+
 // Upper bound of max_query_len (keeps every row and grid count within int).
 constexpr int kMaxQueryLen = 1 << 24;
 
@@ -249,8 +274,30 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, const int32_t* b
   static const int kElementBytes[4] = {4, 2, 2, 1};
   const int64_t block_bytes = (int64_t)h_kv * block_size * head_dim * kElementBytes[kv_dtype];
   if (block_bytes % 16 != 0) return PKV_EUNSUPPORTED;
-  const hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, block_bytes, num_blocks,
-                                               static_cast<hipStream_t>(stream));
+  const hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, block_pairs, num_pairs, block_bytes,
+                                               num_blocks, num_blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* src_k, const void* src_v,
+                    int src_num_blocks, int kv_dtype, const int32_t* block_pairs, int num_pairs, int h_kv,
+                    int head_dim, int block_size, void* stream) {
+  if (num_pairs < 0 || h_kv < 1 || head_dim < 1 || block_size < 1 || dst_num_blocks < 1 || src_num_blocks < 1)
+    return PKV_EINVAL;
+  if (!valid_dtype(kv_dtype)) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !block_pairs) return PKV_EINVAL;
+  static const int kElementBytes[4] = {4, 2, 2, 1};
+  const int64_t block_bytes = (int64_t)h_kv * block_size * head_dim * kElementBytes[kv_dtype];
+  if (block_bytes % 16 != 0) return PKV_EUNSUPPORTED;
+  // every pointer the kernel follows must be memory of this device or pinned
+  // host memory mapped into its address space; anything else is refused here
+  void *dk, *dv, *sk, *sv, *pp;
+  if (!device_address(dst_k, &dk) || !device_address(dst_v, &dv) || !device_address(src_k, &sk) ||
+      !device_address(src_v, &sv) || !device_address(block_pairs, &pp))
+    return PKV_EINVAL;
+  const hipError_t e = pkv::launch_copy_blocks(dk, dv, sk, sv, static_cast<const int32_t*>(pp), num_pairs, block_bytes,
+                                               src_num_blocks, dst_num_blocks, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

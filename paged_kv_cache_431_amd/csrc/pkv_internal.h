@@ -69,7 +69,10 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, int in_d
                                     int num_tokens, int h_kv, int head_dim, int block_size, int num_blocks,
                                     hipStream_t stream);
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int64_t block_bytes,
-                              int num_blocks, hipStream_t stream);
+// Block copies between pools (the same pools for copy-on-write): row i of
+// pairs is (src block, dst block); ids outside their pool are skipped.
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs,
+                              int num_pairs, int64_t block_bytes, int src_blocks, int dst_blocks,
+                              hipStream_t stream);
 
 }  // namespace pkv

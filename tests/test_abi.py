@@ -158,3 +158,20 @@ def test_copy_blocks_rejects_bad_scalars():
     assert call(nb=0) == pkv.PKV_EINVAL
     assert call(kv=3, hkv=1, d=3, bs=1) == pkv.PKV_EUNSUPPORTED   # a 3-byte block
     assert call(n=0) == pkv.PKV_OK                                # nothing to do, nothing launched
+
+
+def test_swap_blocks_rejects_bad_scalars_and_unknown_pointers():
+    L = pkv.lib()
+    P = ctypes.c_void_p
+    call = lambda **o: L.pkv_swap_blocks(P(o.get("dk", 1)), P(1), o.get("dnb", 10), P(1), P(1), o.get("snb", 10),
+                                         o.get("kv", 2), P(o.get("pairs", 1)), o.get("n", 3), 2, o.get("d", 128),
+                                         o.get("bs", 16), None)
+    assert call(n=-1) == pkv.PKV_EINVAL
+    assert call(dnb=0) == pkv.PKV_EINVAL
+    assert call(kv=9) == pkv.PKV_EINVAL
+    assert call(dk=None) == pkv.PKV_EINVAL
+    assert call(pairs=None) == pkv.PKV_EINVAL
+    assert call(kv=3, d=3, bs=1) == pkv.PKV_EUNSUPPORTED     # 6-byte blocks: not whole 16-byte pieces
+    assert call(n=0) == pkv.PKV_OK
+    # addresses the runtime does not know as device or pinned memory
+    assert call() == pkv.PKV_EINVAL
