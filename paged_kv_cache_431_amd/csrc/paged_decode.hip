@@ -354,24 +354,20 @@ __device__ __forceinline__ void mfma_guard() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Two floats holding values exactly representable in CT -> packed CT pair.
-template <int CT>
-__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+// Two E4M3 bytes of w (bytes 0-1, or 2-3 when HI) -> the packed CT pair
+// holding them, lower byte in the low half.  Every E4M3 value is exact in
+// bf16 and in f16, and one gfx950 conversion (scale 1) produces the pair.
+// Only the whole 32-bit result is used: with the toolchain in use, reading
+// element 1 of the builtin's two-element result compiled to a copy of
+// element 0, while the register itself holds both conversions (checked for
+// all 256 codes on the GPU).
+template <int CT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_pair(uint32_t w) {
   if constexpr (CT == kBF16) {
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   } else {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
-}
-
-// Four E4M3 bytes -> four floats (exact).
-__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  f[0] = a[0];
-  f[1] = a[1];
-  f[2] = b[0];
-  f[3] = b[1];
 }
 
 template <int KV, int D>
@@ -481,11 +477,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     for (int kk = 0; kk < NK; ++kk) {
       u32x4 a;
       if constexpr (KV == kFP8) {
-        float f[8];
-        fp8x4_to_f32(r.k[kk >> 1][2 * (kk & 1)], f);
-        fp8x4_to_f32(r.k[kk >> 1][2 * (kk & 1) + 1], f + 4);
-        a = u32x4{pack_exact<CT>(f[0], f[1]), pack_exact<CT>(f[2], f[3]), pack_exact<CT>(f[4], f[5]),
-                  pack_exact<CT>(f[6], f[7])};
+        const uint32_t w0 = r.k[kk >> 1][2 * (kk & 1)], w1 = r.k[kk >> 1][2 * (kk & 1) + 1];
+        a = u32x4{fp8x2_to_pair<CT, false>(w0), fp8x2_to_pair<CT, true>(w0), fp8x2_to_pair<CT, false>(w1),
+                  fp8x2_to_pair<CT, true>(w1)};
       } else {
         a = r.k[kk];
       }
@@ -514,10 +508,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       if constexpr (KV == kFP8) {
 #pragma unroll
         for (int w = 0; w < VDW; ++w) {
-          float f[4];
-          fp8x4_to_f32(r.v[rr][w], f);
-          w16[2 * w] = pack_exact<CT>(f[0], f[1]);
-          w16[2 * w + 1] = pack_exact<CT>(f[2], f[3]);
+          w16[2 * w] = fp8x2_to_pair<CT, false>(r.v[rr][w]);
+          w16[2 * w + 1] = fp8x2_to_pair<CT, true>(r.v[rr][w]);
         }
       } else {
 #pragma unroll

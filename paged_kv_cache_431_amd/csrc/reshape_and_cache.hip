@@ -87,27 +87,49 @@ __device__ __forceinline__ Chunk8<kFP8> quantize8(const Chunk8<IN>& c, float sca
 
 constexpr int kEsize[4] = {4, 2, 2, 1};
 
+// The values' registers are needed here: keeps the compiler from sinking
+// their loads below the slot test (they would then wait for the slot).
+template <int DT>
+__device__ __forceinline__ void issued(const Chunk8<DT>& c) {
+  if constexpr (DT == kF32) {
+    asm volatile("" ::"v"(c.w[0]), "v"(c.w[1]));
+  } else {
+    asm volatile("" ::"v"(c.w));
+  }
+}
+
 template <int IN, int KV>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const uint8_t* key, const uint8_t* value,
                                                                 uint8_t* k_cache, uint8_t* v_cache,
                                                                 const int64_t* slots, int num_tokens, int h_kv,
-                                                                int head_dim, int block_size, int num_blocks,
+                                                                int head_dim, int block_size, int64_t num_slots,
                                                                 float k_scale, float v_scale) {
   const int chunks = head_dim / 8;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)num_tokens * h_kv * chunks) return;
-  const int c = (int)(gid % chunks);
-  const int64_t th = gid / chunks;
-  const int h = (int)(th % h_kv);
-  const int64_t t = th / h_kv;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;  // padding or outside the pool
-  const int64_t blk = slot / block_size;
-  const int64_t off = slot - blk * block_size;
-  const int64_t src = ((t * h_kv + h) * head_dim + (int64_t)c * 8) * kEsize[IN];
-  const int64_t dst = (((blk * h_kv + h) * block_size + off) * head_dim + (int64_t)c * 8) * kEsize[KV];
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;  // the host keeps the thread count below 2^31
+  if (gid >= num_tokens * h_kv * chunks) return;
+  const int c = gid % chunks;
+  const int th = gid / chunks;
+  const int h = th % h_kv;
+  const int t = th / h_kv;
+  // the token's K/V do not depend on its slot: their loads go out together
+  // with the slot's, so the chain is two round trips (loads, then stores)
+  const int64_t src = ((int64_t)th * head_dim + (int64_t)c * 8) * kEsize[IN];
   const Chunk8<IN> kin = load8<IN>(key + src);
   const Chunk8<IN> vin = load8<IN>(value + src);
+  const int64_t slot = slots[t];
+  issued<IN>(kin);
+  issued<IN>(vin);
+  if (slot < 0 || slot >= num_slots) return;  // padding or outside the pool
+  int64_t blk, off;
+  if (num_slots <= 0x7fffffff) {  // the common pool: 32-bit division
+    const int s32 = (int)slot;
+    blk = s32 / block_size;
+    off = s32 - (int)blk * block_size;
+  } else {
+    blk = slot / block_size;
+    off = slot - blk * block_size;
+  }
+  const int64_t dst = (((blk * h_kv + h) * block_size + off) * head_dim + (int64_t)c * 8) * kEsize[KV];
   if constexpr (IN == KV) {
     store8<KV>(k_cache + dst, kin);
     store8<KV>(v_cache + dst, vin);
@@ -122,10 +144,11 @@ hipError_t launch(const void* key, const void* value, void* kc, void* vc, const 
                   int d, int bs, int nb, float ks, float vs, hipStream_t stream) {
   const int64_t threads = (int64_t)T * h_kv * (d / 8);
   if (threads == 0) return hipSuccess;
+  if (threads > 0x7fffff00) return hipErrorInvalidValue;
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((reshape_and_cache_kernel<IN, KV>), dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value), static_cast<uint8_t*>(kc),
-                     static_cast<uint8_t*>(vc), slots, T, h_kv, d, bs, nb, ks, vs);
+                     static_cast<uint8_t*>(vc), slots, T, h_kv, d, bs, (int64_t)nb * bs, ks, vs);
   return hipGetLastError();
 }
 
