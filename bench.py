@@ -2,14 +2,15 @@
 
 A step is one decode step of the 70B-style GQA model the pages size (80 layers,
 8 KV heads of 128 dims, bf16): for each of 80 layers, the new tokens' K/V are
-scattered into that layer's paged pool (reshape_and_cache) and paged decode
-attention runs over it.  Each layer has its own pool of 2,457 blocks (the
+scattered into that layer's paged pool and paged decode attention runs over
+it, in one launch per layer (pkv_decode_step; two_launch_step times the
+separate reshape_and_cache and decode calls for the same work).  Each layer has its own pool of 2,457 blocks (the
 12 GiB budget of the pages split over 80 layers), so a step streams about
 12.7 GB of KV and repeats never hit in the 256 MB last-level cache.
 
 value = KV bytes a step must read (sum over sequences of context_len x 2 x
 h_kv x head_dim x 2 B, x 80 layers) / step time, in GB/s.
-roofline = the decode kernel alone: the same bytes per launch / its mean
+roofline = the step's attention kernel alone: the same bytes per launch / its mean
 launch duration (HIP events on its stream around back-to-back launches over
 the layer pools); traffic = HBM bytes per launch from rocprofv3 counters,
 reported only while the kernel source is the one they were taken on.
@@ -52,8 +53,9 @@ MULTI_TOKENS = 4
 
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("ab32f66652a4ae393ae288e82ccd4a34bc14b34f2d42818a1a1ffb1af737e1d1", "gqa70b-bf16-47x825", 1): 162697421,
-    ("ab32f66652a4ae393ae288e82ccd4a34bc14b34f2d42818a1a1ffb1af737e1d1", "gqa70b-bf16-47x825-multi4", 1): 171542733,
+    ("74a6b64ba27bad05536f93448511ad0f9f5b16f474c12dd430963d88ad82875d", "gqa70b-bf16-47x825-step", 1): 163106762,
+    ("74a6b64ba27bad05536f93448511ad0f9f5b16f474c12dd430963d88ad82875d", "gqa70b-bf16-47x825", 1): 162696112,
+    ("74a6b64ba27bad05536f93448511ad0f9f5b16f474c12dd430963d88ad82875d", "gqa70b-bf16-47x825-multi4", 1): 171601947,
 }
 
 
@@ -235,46 +237,73 @@ def main():
                                                   stream=stream) for t in pools]
     scatters = [pkv.prepare_reshape_and_cache(t.new_k, t.new_v, t.k_cache, t.v_cache, slots, k_scale=t.k_scale,
                                               v_scale=t.v_scale, stream=stream) for t in pools]
-    layer_calls = list(zip(scatters, decodes))
+    two_launch_calls = [c for pair in zip(scatters, decodes) for c in pair]
+    # One launch per layer where the library fuses the scatter into decode
+    # (matrix-core configurations), the two calls otherwise: the same bits.
+    fused = True
+    try:
+        steps_fused = [pkv.prepare_decode_step(out, t.q, t.new_k, t.new_v, t.k_cache, t.v_cache, tables, lens,
+                                               max_context_len=plan.max_context_len, workspace=ws, k_scale=t.k_scale,
+                                               v_scale=t.v_scale, num_splits=args.splits, stream=stream)
+                       for t in pools]
+        steps_fused[0]()
+    except pkv.PkvError as e:
+        if e.status != pkv.PKV_EUNSUPPORTED:
+            raise
+        fused, steps_fused = False, []
+    layer_calls = steps_fused if fused else two_launch_calls
+    kernel_calls = steps_fused if fused else decodes
 
-    def step():
-        for scatter, decode in layer_calls:
-            scatter()
-            decode()
+    def time_step(calls):
+        for _ in range(args.warmup):
+            for call in calls:
+                call()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            for call in calls:
+                call()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step = time_step(layer_calls)
+    ms_two = time_step(two_launch_calls) if fused else ms_step
 
-    # The decode kernel alone: L back-to-back launches (one per layer pool)
-    # between one event pair on the kernel's stream, repeated; the mean launch
-    # duration is the total over the launches.  An event pair around each
-    # single launch is also kept (it adds the event and dispatch overhead).
+    # The step's attention kernel alone: L back-to-back launches (one per
+    # layer pool) between one event pair on the kernel's stream, repeated;
+    # the mean launch duration is the total over the launches.  An event pair
+    # around each single launch is also kept (it adds the event and dispatch
+    # overhead).
     reps = max(1, min(5, args.steps))
     batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in batch:
         a.record(stream)
-        for decode in decodes:
-            decode()
+        for call in kernel_calls:
+            call()
         b.record(stream)
     torch.cuda.synchronize()
     mean_launch_ms = sum(a.elapsed_time(b) for a, b in batch) / (reps * L)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * L)]
     for r in range(reps):
-        for l, decode in enumerate(decodes):
+        for l, call in enumerate(kernel_calls):
             a, b = evs[r * L + l]
             a.record(stream)
-            decode()
+            call()
             b.record(stream)
     torch.cuda.synchronize()
     launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    decode_only_ms = mean_launch_ms
+    if fused:  # the plain decode kernel over the same pools, for comparison
+        batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in batch:
+            a.record(stream)
+            for call in decodes:
+                call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        decode_only_ms = sum(a.elapsed_time(b) for a, b in batch) / (reps * L)
 
     per_call = kv_bytes_per_call(plan)
     step_bytes = per_call * L
@@ -300,15 +329,20 @@ def main():
                    "q_dtype": wl.q_dtype, "pool_blocks_per_layer": plan.num_blocks, "num_splits": n_splits,
                    "kv_bytes_per_layer_call": per_call, "kv_bytes_per_step": step_bytes},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "launches_per_layer": 1 if fused else 2,
+        "two_launch_step": {"ms_per_step": round(ms_two, 4), "value": round(step_bytes / (ms_two * 1e-3) / 1e9, 2),
+                            "note": "pkv_reshape_and_cache then pkv_paged_attention_decode per layer"},
         "seqs_per_s": round(wl.num_seqs / (ms_step * 1e-3 / L), 1),
         "decode_steps_per_s": round(1000.0 / ms_step, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(wl.name, n_splits),
-                     "kernel": "decode_mfma_kernel" if wl.kv_dtype != "f32" else "decode_vector_kernel",
+                     "traffic": measured_traffic(wl.name + ("-step" if fused else ""), n_splits),
+                     "kernel": ("decode_mfma_kernel (decode step, new tokens written in-kernel)" if fused else
+                                "decode_mfma_kernel" if wl.kv_dtype != "f32" else "decode_vector_kernel"),
                      "mean_launch_us": round(mean_launch_ms * 1e3, 3),
                      "isolated_launch_median_us": round(launch_ms[len(launch_ms) // 2] * 1e3, 3),
-                     "algorithmic_bytes_per_launch": per_call},
+                     "algorithmic_bytes_per_launch": per_call,
+                     "decode_only_mean_launch_us": round(decode_only_ms * 1e3, 3)},
     }
     # copy-on-write block copy: disjoint (src, dst) block pairs of one layer pool
     n_pairs = min(1024, plan.num_blocks // 2)
@@ -362,7 +396,7 @@ def main():
         "frac_of_hbm_peak": round(per_call / (multi_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     result["swap_blocks"] = swap_measurement(pkv, pools[0], plan, wl, stream, n_pairs, HBM_PEAK_GBS)
     if not args.no_cpu_baseline:
-        del pools, decodes, scatters, layer_calls, multis
+        del pools, decodes, scatters, layer_calls, multis, steps_fused, two_launch_calls, kernel_calls
         torch.cuda.empty_cache()
         fresh = workloads.make_tensors(plan, rp, device=dev, poison=False, pool_seed_offset=0)  # untouched by HIP
         result["cpu_baseline"] = cpu_baseline(plan, rp, fresh, args.cpu_budget)

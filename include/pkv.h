@@ -130,6 +130,34 @@ int pkv_paged_attention_decode(void* out, int out_dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * One decode step in one launch: each sequence's new token is written into
+ * its slot and attention runs over the context that includes it.
+ *
+ * Same result, bit for bit, as pkv_reshape_and_cache of new_k / new_v into
+ * the slots of positions context_lens[s] - 1 followed by
+ * pkv_paged_attention_decode, without the separate launch: the workgroup
+ * that reads a sequence's last position writes the new token there itself,
+ * and uses the rows it wrote for that position.
+ *   new_k, new_v  [S, Hkv, D] in new_dtype: the K/V of each sequence's new
+ *                 token, which is position context_lens[s] - 1 (its slot
+ *                 comes from block_tables; the block holding it must not be
+ *                 shared with another sequence, which copy-on-write ensures).
+ *                 new_dtype == kv_dtype copies the bits; an FP8_E4M3 pool
+ *                 takes F32 / F16 / BF16 with the scatter's rounding
+ *                 (x / k_scale or x / v_scale).  A sequence with context
+ *                 length 0 has no new token and gets output 0.
+ *   other arguments as for pkv_paged_attention_decode (same workspace).
+ * Supported: the matrix-core combinations of decode; others return
+ *   PKV_EUNSUPPORTED (use the two calls).  Errors as for decode, plus
+ *   PKV_EINVAL for NULL new_k / new_v with S > 0.
+ * ------------------------------------------------------------------------ */
+int pkv_decode_step(void* out, int out_dtype, const void* q, int q_dtype, const void* new_k, const void* new_v,
+                    int new_dtype, void* k_cache, void* v_cache, int kv_dtype, float k_scale, float v_scale,
+                    const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
+                    int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+                    float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Paged attention for several new query tokens per sequence (a chunk of a
  * prompt recomputed over a cached prefix, or the lookahead tokens of
  * speculative decoding), with a causal mask.

@@ -11,6 +11,7 @@ HIP stream to the C ABI declared in include/pkv.h (same function names).
 
   pkv_paged_attention_decode   paged decode attention (one launch)
   pkv_paged_attention_multi    several new query tokens per sequence, causal
+  pkv_decode_step              scatter of the new tokens + decode in one launch
   pkv_reshape_and_cache        write new tokens' K/V into their slots
   pkv_copy_blocks              copy blocks (src -> dst) in both pools: copy-on-write
   pkv_swap_blocks              move blocks between a device pool and a pinned host pool
@@ -64,6 +65,9 @@ def lib():
         "pkv_paged_attention_decode": (c_int, [c_p, c_int, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_p,
                                                c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_f, c_int,
                                                c_p, c_sz, c_p]),
+        "pkv_decode_step": (c_int, [c_p, c_int, c_p, c_int, c_p, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_p,
+                                    c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_f, c_int, c_p, c_sz,
+                                    c_p]),
         "pkv_multi_workspace_bytes": (c_sz, [c_int] * 8),
         "pkv_multi_num_splits": (c_int, [c_int] * 8),
         "pkv_paged_attention_multi": (c_int, [c_p, c_int, c_p, c_int, c_p, c_int, c_int, c_p, c_p, c_int, c_f, c_f,
@@ -231,6 +235,45 @@ def pkv_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_le
     return out
 
 
+def _step_args(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace, scale,
+               k_scale, v_scale, num_splits, stream):
+    import torch
+    S, h_q, D = q.shape
+    NB, h_kv, B, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (S, h_q, D):
+        raise ValueError("shape mismatch between q / out / k_cache / v_cache")
+    if tuple(new_k.shape) != (S, h_kv, D) or new_v.shape != new_k.shape or new_v.dtype != new_k.dtype:
+        raise ValueError("new_k and new_v must be [S, Hkv, D] of one dtype")
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must share a dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    return (_dev_ptr(out, "out"), dtype_code(out), _dev_ptr(q, "q"), dtype_code(q), _dev_ptr(new_k, "new_k"),
+            _dev_ptr(new_v, "new_v"), dtype_code(new_k), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+            dtype_code(k_cache), float(k_scale), float(v_scale), _dev_ptr(block_tables, "block_tables"),
+            _dev_ptr(context_lens, "context_lens"), S, h_q, h_kv, D, B, NB, block_tables.shape[1],
+            int(max_context_len), float(scale), int(num_splits), _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def pkv_decode_step(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
+                    scale=0.0, k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+    """One decode step in one launch: new_k / new_v [S, Hkv, D] go to position
+    context_lens[s] - 1 of each sequence (slot from its block table), then
+    out[s, g, :] is the attention of q[s, g, :] over the context including
+    it.  Same bits as pkv_reshape_and_cache followed by the decode call."""
+    if workspace is None:
+        S, h_q, D = q.shape
+        workspace = make_workspace(S, h_q, k_cache.shape[1], D, k_cache.shape[2], max_context_len, num_splits,
+                                   device=q.device)
+    args = _step_args(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace,
+                      scale, k_scale, v_scale, num_splits, stream)
+    _check(lib().pkv_decode_step(*args), "pkv_decode_step")
+    return out
+
+
 class PreparedCall:
     """A C-ABI call whose arguments were validated and marshalled once.
 
@@ -271,6 +314,15 @@ def prepare_paged_attention_multi(out, q, k_cache, v_cache, block_tables, contex
                        max_context_len, workspace, scale, k_scale, v_scale, num_splits, stream)
     return PreparedCall(lib().pkv_paged_attention_multi, args, "pkv_paged_attention_multi",
                         (out, q, k_cache, v_cache, block_tables, context_lens, query_start, workspace))
+
+
+def prepare_decode_step(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
+                        workspace, scale=0.0, k_scale=1.0, v_scale=1.0, num_splits=0, stream=None):
+    """PreparedCall of pkv_decode_step (same arguments)."""
+    args = _step_args(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace,
+                      scale, k_scale, v_scale, num_splits, stream)
+    return PreparedCall(lib().pkv_decode_step, args, "pkv_decode_step",
+                        (out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, workspace))
 
 
 def prepare_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, *, k_scale=1.0, v_scale=1.0, stream=None):

@@ -102,12 +102,13 @@ int resolve_multi_splits(int num_seqs, int h_q, int h_kv, int max_query_len, int
 // Decode (query_start == nullptr: one query token per sequence) and calls
 // with several query tokens per sequence share validation and launch.
 int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
-                  int num_query_tokens, int max_query_len, const void* k_cache, const void* v_cache, int kv_dtype,
-                  float k_scale, float v_scale, const int32_t* block_tables, const int32_t* context_lens,
-                  int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int num_blocks,
-                  int max_blocks_per_seq, int max_context_len, float scale, int num_splits, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  int num_query_tokens, int max_query_len, const void* new_k, const void* new_v, int new_dtype,
+                  const void* k_cache, const void* v_cache, int kv_dtype, float k_scale, float v_scale,
+                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
+                  int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+                  float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   const bool multi = query_start != nullptr;
+  const bool append = new_k != nullptr;
   if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return PKV_EINVAL;
   if (num_blocks < 1 || max_blocks_per_seq < 1) return PKV_EINVAL;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_EINVAL;
@@ -131,6 +132,12 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   const bool matrix_core = kv_dtype != PKV_F32 && block_size % pkv::kTileTokens == 0 &&
                            (tiles_per_block & (tiles_per_block - 1)) == 0;
   if (multi && !matrix_core) return PKV_EUNSUPPORTED;
+  if (append) {
+    if (!matrix_core) return PKV_EUNSUPPORTED;
+    if (!valid_dtype(new_dtype)) return PKV_EINVAL;
+    const bool enc_ok = new_dtype == kv_dtype || (kv_dtype == PKV_FP8_E4M3 && new_dtype != PKV_FP8_E4M3);
+    if (!enc_ok) return PKV_EUNSUPPORTED;
+  }
 
   const int n = multi ? resolve_multi_splits(num_seqs, h_q, h_kv, max_query_len, max_context_len, num_splits)
                       : resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
@@ -170,6 +177,11 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   a.query_start = query_start;
   a.num_query_tokens = multi ? num_query_tokens : 0;
   a.max_query_len = multi ? max_query_len : 1;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.new_dtype = new_dtype;
+  a.k_scale_enc = k_scale;
+  a.v_scale_enc = v_scale;
   const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
@@ -211,9 +223,22 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, int q_dt
                                int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                                int max_context_len, float scale, int num_splits, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  return run_attention(out, out_dtype, q, q_dtype, nullptr, 0, 1, k_cache, v_cache, kv_dtype, k_scale, v_scale,
-                       block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, max_context_len, scale, num_splits, workspace, workspace_bytes, stream);
+  return run_attention(out, out_dtype, q, q_dtype, nullptr, 0, 1, nullptr, nullptr, 0, k_cache, v_cache, kv_dtype,
+                       k_scale, v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, num_splits, workspace,
+                       workspace_bytes, stream);
+}
+
+int pkv_decode_step(void* out, int out_dtype, const void* q, int q_dtype, const void* new_k, const void* new_v,
+                    int new_dtype, void* k_cache, void* v_cache, int kv_dtype, float k_scale, float v_scale,
+                    const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
+                    int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+                    float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!new_k || !new_v)) return PKV_EINVAL;
+  return run_attention(out, out_dtype, q, q_dtype, nullptr, 0, 1, num_seqs > 0 ? new_k : nullptr, new_v, new_dtype,
+                       k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables, context_lens, num_seqs, h_q,
+                       h_kv, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                       num_splits, workspace, workspace_bytes, stream);
 }
 
 int pkv_multi_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
@@ -240,10 +265,10 @@ int pkv_paged_attention_multi(void* out, int out_dtype, const void* q, int q_dty
     return PKV_EINVAL;
   if (num_query_tokens < 0) return PKV_EINVAL;
   if (num_seqs > 0 && !query_start) return PKV_EINVAL;
-  return run_attention(out, out_dtype, q, q_dtype, query_start, num_query_tokens, max_query_len, k_cache, v_cache,
-                       kv_dtype, k_scale, v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim,
-                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, num_splits, workspace,
-                       workspace_bytes, stream);
+  return run_attention(out, out_dtype, q, q_dtype, query_start, num_query_tokens, max_query_len, nullptr, nullptr, 0,
+                       k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables, context_lens, num_seqs, h_q, h_kv,
+                       head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, num_splits,
+                       workspace, workspace_bytes, stream);
 }
 
 int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype, void* k_cache, void* v_cache,

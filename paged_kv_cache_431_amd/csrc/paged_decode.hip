@@ -67,6 +67,7 @@
 // reductions.
 
 #include "device_common.h"
+#include "kv_chunk.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -98,6 +99,15 @@ struct Params {
   const int32_t* query_start;
   int num_query_tokens, max_query_len;
   int row_tiles;  // 16-row tiles of (query token, head) rows per (sequence, KV head)
+  // Decode step that appends each sequence's new token itself (null
+  // otherwise): new_k, new_v [S, h_kv, D] in new_dtype go to position ctx - 1
+  // (its slot from the block table), converted as the scatter converts.
+  const uint8_t* new_k;
+  const uint8_t* new_v;
+  uint8_t* k_store;
+  uint8_t* v_store;
+  int new_dtype;
+  float k_scale_enc, v_scale_enc;
 };
 
 struct Item {
@@ -114,11 +124,17 @@ struct Item {
 // Query token i of the m new tokens of a sequence with ctx cached tokens
 // (its own K/V included) sits at position ctx - m + i and attends to the
 // positions up to and including its own.
+// Workgroup id -> unit index (decode: the (sequence, KV head) index).
+__device__ __forceinline__ int decode_unit(const Params& p) {
+  const int wg = blockIdx.x;
+  return ((wg >> 3) / p.num_splits) * 8 + (wg & 7);
+}
+
 template <bool MT>
 __device__ __forceinline__ bool get_item(const Params& p, Item& it) {
   const int wg = blockIdx.x;
   const int j = wg >> 3;
-  it.unit = (j / p.num_splits) * 8 + (wg & 7);
+  it.unit = decode_unit(p);
   it.split = j % p.num_splits;
   int base = it.unit;  // (sequence, KV head) index
   it.rt = 0;
@@ -389,7 +405,7 @@ struct MfmaTile {
   int tok0;  // position of its first token
 };
 
-template <int KV, int CT, int D, bool MT>
+template <int KV, int CT, int D, bool MT, bool AP>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd))) void decode_mfma_kernel(
     Params p) {
   using Tile = MfmaTile<KV, D>;
@@ -402,11 +418,41 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int VCH = D / 8;  // 16-byte chunks in a 16-bit V row
 
   __shared__ union {
-    // per-wave V tile of 16 tokens in its natural [token][d] layout, 16-bit
-    // elements, 16-byte chunks of each row XOR-swizzled by the row
-    u32x4 vtile[kDecodeWaves][kTileTokens * VCH];
+    struct {
+      // per-wave V tile of 16 tokens in its natural [token][d] layout, 16-bit
+      // elements, 16-byte chunks of each row XOR-swizzled by the row
+      u32x4 vtile[kDecodeWaves][kTileTokens * VCH];
+      // decode step: the new token's K and V rows as stored in the pools, one
+      // copy per wave (each wave stages its own: no barrier)
+      uint8_t newrow[kDecodeWaves][2][ROW];
+    } t;
     MergeSmem<D> merge;
   } sm;
+
+  // Decode step: the new token's K and V rows of this (sequence, KV head) do
+  // not depend on the context length, so every wave loads them first and
+  // they arrive with it (the wave that turns out to own the last position
+  // uses them).  Lane l < 2 CH holds 8 elements (K chunks, then V chunks); every
+  // lane loads (the others repeat the last chunk), so the compiler counts
+  // this load with the ones after it.
+  constexpr int CH = D / 8;
+  c8_u32x4 nraw0 = {0u, 0u, 0u, 0u}, nraw1 = {0u, 0u, 0u, 0u};
+  if constexpr (AP) {
+    const int l = min((int)(threadIdx.x & 63), 2 * CH - 1);
+    const bool is_v = l >= CH;
+    const int unit = min(decode_unit(p), p.units - 1);
+    const size_t elem = (size_t)unit * D + (is_v ? l - CH : l) * 8;  // rows are [S, h_kv] in unit order
+    const uint8_t* src = is_v ? p.new_v : p.new_k;
+    if (p.new_dtype == kF32) {
+      nraw0 = *reinterpret_cast<const c8_u32x4*>(src + elem * 4);
+      nraw1 = *reinterpret_cast<const c8_u32x4*>(src + elem * 4 + 16);
+    } else if (p.new_dtype == kFP8) {
+      const c8_u32x2 x = *reinterpret_cast<const c8_u32x2*>(src + elem);
+      nraw0 = c8_u32x4{x[0], x[1], 0u, 0u};
+    } else {
+      nraw0 = *reinterpret_cast<const c8_u32x4*>(src + elem * 2);
+    }
+  }
 
   Item it;
   if (!get_item<MT>(p, it)) return;
@@ -452,6 +498,40 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
+  // the new token's rows converted to the pool's element type, into the
+  // owner wave's LDS copy (K row, then V row)
+  auto stage_new_token = [&]() {
+    if (lane < 2 * CH) {
+      const bool is_v = lane >= CH;
+      uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][(is_v ? lane - CH : lane) * 8 * Tile::ES];
+      if constexpr (KV == kFP8) {
+        const float enc = is_v ? p.v_scale_enc : p.k_scale_enc;
+        Chunk8<kFP8> x;
+        if (p.new_dtype == kF32) {
+          Chunk8<kF32> c;
+          c.w[0] = nraw0;
+          c.w[1] = nraw1;
+          x = quantize8<kF32>(c, enc);
+        } else if (p.new_dtype == kF16) {
+          Chunk8<kF16> c;
+          c.w = nraw0;
+          x = quantize8<kF16>(c, enc);
+        } else if (p.new_dtype == kBF16) {
+          Chunk8<kBF16> c;
+          c.w = nraw0;
+          x = quantize8<kBF16>(c, enc);
+        } else {
+          x.w = c8_u32x2{nraw0[0], nraw0[1]};
+        }
+        store8<kFP8>(stage, x);
+      } else {
+        Chunk8<KV> x;
+        x.w = nraw0;
+        store8<KV>(stage, x);
+      }
+    }
+  };
+
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -469,8 +549,34 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const uint8_t* kbase = p.k_cache + it.kvh * head_bytes + lo16 * ROW + q4 * 16;
   const uint8_t* vbase = p.v_cache + it.kvh * head_bytes + (4 * q4) * ROW + lo16 * Tile::VB;
 
+  // Decode step: the wave whose tiles include the sequence's last position
+  // (the last tile of the last split) appends the new token: it computes
+  // that tile with the new rows (staged in LDS at the start) in place of the
+  // loaded ones, and writes them to the pool after its last tile.  No other
+  // wave or workgroup reads that position, so nothing waits for the write.
+  const bool owner = AP && it.t_end == it.n_tiles && wb <= it.n_tiles - 1 && it.n_tiles - 1 < wb + n_my;
+  const int last_tok0 = (it.n_tiles - 1) * kTileTokens;
+  int last_phys = -1;  // physical block of the last position (owner wave)
+
   auto compute_tile = [&](Tile& r, bool valid) {
     const int lim = valid ? r.lim : 0;
+    if constexpr (AP) {
+      if (owner && valid && r.tok0 == last_tok0) {  // the tile holding the new token (wave-uniform)
+        const int row = it.ctx - 1 - r.tok0;
+        if (lo16 == row) {
+#pragma unroll
+          for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(&sm.t.newrow[wave][0][q4 * 16 + c * 64]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          if (4 * q4 + rr == row) {
+#pragma unroll
+            for (int w = 0; w < VDW; ++w)
+              r.v[rr][w] = *reinterpret_cast<const uint32_t*>(&sm.t.newrow[wave][1][lo16 * Tile::VB + 4 * w]);
+          }
+        }
+      }
+    }
     // 1) scores for the 16 tokens of the tile against the (padded) query group
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -500,7 +606,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     // Row t of the tile, 16-byte chunk c sits at chunk c ^ swz(t) of row t:
     // the transposed reads below then touch all banks evenly.
     auto vt_chunk = [&](int t, int c) { return t * VCH + (c ^ ((t & (VCH / 2 - 1)) << 1)); };
-    u32x4* vt = sm.vtile[wave];
+    u32x4* vt = sm.t.vtile[wave];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int t = 4 * q4 + rr;  // this lane holds d = lo16 * D/16 ... of row t
@@ -610,6 +716,11 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     // Lane j holds the physical block of tile t0 + j (clamped into the chunk,
     // so only table entries of blocks the context covers are read).
     const int ids = bt_row[(t0 + min(lane, cn - 1)) >> p.tile_shift];
+    // decode step: the owner stages the new token here, where the wave waits
+    // for the block ids anyway (that load is the youngest)
+    if constexpr (AP) {
+      if (c0 == 0 && owner) stage_new_token();
+    }
 
     auto load_tile = [&](Tile& r, int j) {  // j: tile of the chunk, 0 <= j < cn (wave-uniform)
       const int tok0 = (t0 + j) * kTileTokens;
@@ -652,11 +763,32 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       // tile never waits for a younger one
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (AP) {
+      if (owner && c0 + cn == n_my) last_phys = __builtin_amdgcn_readlane(ids, cn - 1);
+    }
     for (int i = 0; i < cn; i += NBUF) {
 #pragma unroll
       for (int b = 0; b < NBUF; ++b) {
         load_tile(buf[(b + NBUF - 1) % NBUF], min(i + b + NBUF - 1, cn - 1));
         compute_tile(buf[b], i + b < cn);
+      }
+    }
+  }
+
+  if constexpr (AP) {
+    // the new token into its slot (its rows are still in LDS)
+    if (owner && (unsigned)last_phys < (unsigned)p.num_blocks && lane < 2 * CH) {
+      const bool is_v = lane >= CH;
+      const int c = is_v ? lane - CH : lane;
+      const int pos = it.ctx - 1;
+      const int off = pos - (pos / p.block_size) * p.block_size;
+      const size_t dst = (((size_t)last_phys * p.h_kv + it.kvh) * p.block_size + off) * ROW + c * 8 * Tile::ES;
+      const uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][c * 8 * Tile::ES];
+      uint8_t* cache = (is_v ? p.v_store : p.k_store) + dst;
+      if constexpr (KV == kFP8) {
+        store8<kFP8>(cache, load8<kFP8>(stage));
+      } else {
+        store8<KV>(cache, load8<KV>(stage));
       }
     }
   }
@@ -776,23 +908,27 @@ hipError_t launch(K kernel, int grid, const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool MT>
+template <int D, bool MT, bool AP>
 hipError_t dispatch_mfma(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
-  if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kBF16, kBF16, D, MT>, grid, p, s);
-  if (a.kv_dtype == kF16 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kF16, kF16, D, MT>, grid, p, s);
-  if (a.kv_dtype == kFP8 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kFP8, kBF16, D, MT>, grid, p, s);
-  if (a.kv_dtype == kFP8 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kFP8, kF16, D, MT>, grid, p, s);
+  if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP>, grid, p, s);
+  if (a.kv_dtype == kF16 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP>, grid, p, s);
+  if (a.kv_dtype == kFP8 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP>, grid, p, s);
+  if (a.kv_dtype == kFP8 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP>, grid, p, s);
   return hipErrorInvalidValue;
 }
 
 template <int D>
 hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
   if (a.query_start != nullptr) {
+    if (!a.matrix_core || a.new_k != nullptr) return hipErrorInvalidValue;
+    return dispatch_mfma<D, true, false>(a, grid, p, s);
+  }
+  if (a.new_k != nullptr) {
     if (!a.matrix_core) return hipErrorInvalidValue;
-    return dispatch_mfma<D, true>(a, grid, p, s);
+    return dispatch_mfma<D, false, true>(a, grid, p, s);
   }
   if (a.matrix_core) {
-    return dispatch_mfma<D, false>(a, grid, p, s);
+    return dispatch_mfma<D, false, false>(a, grid, p, s);
   } else {
     if (a.kv_dtype == kF32 && a.q_dtype == kF32) return launch(decode_vector_kernel<kF32, kF32, D>, grid, p, s);
     if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_vector_kernel<kBF16, kBF16, D>, grid, p, s);
@@ -863,6 +999,13 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.num_query_tokens = a.num_query_tokens;
   p.max_query_len = a.max_query_len;
   p.row_tiles = row_tiles;
+  p.new_k = static_cast<const uint8_t*>(a.new_k);
+  p.new_v = static_cast<const uint8_t*>(a.new_v);
+  p.k_store = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
+  p.v_store = static_cast<uint8_t*>(const_cast<void*>(a.v_cache));
+  p.new_dtype = a.new_dtype;
+  p.k_scale_enc = a.k_scale_enc;
+  p.v_scale_enc = a.v_scale_enc;
   const int grid = ((p.units + 7) / 8) * 8 * row_tiles * a.num_splits;
   if (grid == 0) return hipSuccess;
   if (a.head_dim == 128) return dispatch<128>(a, grid, p, stream);

@@ -40,6 +40,14 @@ struct DecodeLaunch {
   // sequence s are [query_start[s], query_start[s + 1]), at most max_query_len.
   const int32_t* query_start;
   int num_query_tokens, max_query_len;
+  // Decode step that appends the new tokens itself (new_k != nullptr;
+  // matrix-core path, one query token): new_k, new_v [num_seqs, h_kv,
+  // head_dim] in new_dtype are written to position context_lens[s] - 1, FP8
+  // pools dividing by k_scale_enc / v_scale_enc as the scatter does.
+  const void* new_k;
+  const void* new_v;
+  int new_dtype;
+  float k_scale_enc, v_scale_enc;
 };
 
 // 16-row tiles of (query token, query head) rows per (sequence, KV head).

@@ -175,3 +175,20 @@ def test_swap_blocks_rejects_bad_scalars_and_unknown_pointers():
     assert call(n=0) == pkv.PKV_OK
     # addresses the runtime does not know as device or pinned memory
     assert call() == pkv.PKV_EINVAL
+
+
+def test_decode_step_rejects_bad_arguments_without_launching():
+    # every call below fails validation before anything is launched (the
+    # pointers are not real)
+    L = pkv.lib()
+    P = ctypes.c_void_p
+    call = lambda **o: L.pkv_decode_step(P(1), 0, P(1), 2, P(o.get("nk", 1)), P(1), o.get("nd", 2), P(1), P(1),
+                                         o.get("kv", 2), 1.0, 1.0, P(1), P(1), o.get("S", 4), 8, 2, 128,
+                                         o.get("bs", 16), 10, 4, 64, 0.0, 0, P(1), o.get("wsb", 16), None)
+    assert call(nk=None) == pkv.PKV_EINVAL
+    assert call(nd=7) == pkv.PKV_EINVAL
+    assert call(nd=1) == pkv.PKV_EUNSUPPORTED                # f16 tokens into a bf16 pool
+    assert call(nd=2, kv=0, wsb=1 << 30) == pkv.PKV_EUNSUPPORTED  # fp32 pool: vector path, no fused step
+    assert call(bs=8, wsb=1 << 30) == pkv.PKV_EINVAL         # 64 tokens do not fit 4 blocks of 8
+    assert call(wsb=16) == pkv.PKV_EWORKSPACE
+    assert call(S=0, nk=None) == pkv.PKV_OK
