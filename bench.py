@@ -41,10 +41,10 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "gqa70b-bf16-47x825"
 
 
-# HBM bytes per decode launch from rocprofv3 counters (FETCH_SIZE x 2 +
-# WRITE_SIZE: on a 1 GiB device copy FETCH_SIZE reads half the bytes read and
-# WRITE_SIZE all the bytes written), valid only for the kernel source they
-# were taken on (its SHA-256) and the workload / split count they ran.
+# HBM bytes per launch from rocprofv3 counters (FETCH_SIZE x 2 + WRITE_SIZE:
+# on a 1 GiB device copy FETCH_SIZE reads half the bytes read and WRITE_SIZE
+# all the bytes written), valid only for the kernel code they were taken on
+# (kernel_source_sha256) and the workload / split count they ran.
 # Host link of an MI355X: PCIe 5.0 x16, per direction.
 PCIE_PEAK_GBS = 64.0
 
@@ -53,17 +53,26 @@ MULTI_TOKENS = 4
 
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("74a6b64ba27bad05536f93448511ad0f9f5b16f474c12dd430963d88ad82875d", "gqa70b-bf16-47x825-step", 1): 163106762,
-    ("74a6b64ba27bad05536f93448511ad0f9f5b16f474c12dd430963d88ad82875d", "gqa70b-bf16-47x825", 1): 162696112,
-    ("74a6b64ba27bad05536f93448511ad0f9f5b16f474c12dd430963d88ad82875d", "gqa70b-bf16-47x825-multi4", 1): 171601947,
+    ("a83c03b34497eae8224cb4a9cea3d917f29313352d3ce6fc711b8bf21db3c561", "gqa70b-bf16-47x825-step", 1): 163106762,
+    ("a83c03b34497eae8224cb4a9cea3d917f29313352d3ce6fc711b8bf21db3c561", "gqa70b-bf16-47x825", 1): 162696112,
+    ("a83c03b34497eae8224cb4a9cea3d917f29313352d3ce6fc711b8bf21db3c561", "gqa70b-bf16-47x825-multi4", 1): 171601947,
 }
 
 
 def kernel_source_sha256():
+    """SHA-256 of the attention kernels' code: paged_decode.hip with its //
+    comments, blank lines and runs of white space removed, so that editing a
+    comment does not invalidate counters taken on the same code."""
     import hashlib
+    import re
     path = os.path.join(ROOT, "paged_kv_cache_431_amd", "csrc", "paged_decode.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    lines = []
+    with open(path) as f:
+        for line in f:
+            line = re.sub(r"//.*$", "", line).strip()
+            if line:
+                lines.append(re.sub(r"\s+", " ", line))
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def measured_traffic(workload, num_splits):

@@ -1,6 +1,6 @@
-// Paged decode attention for gfx950 (MI355X).
+// Paged attention for gfx950 (MI355X).
 //
-// The attention of one new query token per sequence over that sequence's
+// The attention of a sequence's new query token(s) over that sequence's
 // cached K/V, read block by block through the sequence's block table, never
 // gathered into a contiguous copy ("KV cache and PagedAttention in serving",
 // section "PagedAttention: virtual memory for GPUs"; "Paged KV Cache"
@@ -29,7 +29,7 @@
 //   compiler can wait for exactly the oldest tile instead of draining every
 //   outstanding load.
 //
-// Matrix-core path (16-bit or FP8 caches, block_size a multiple of 16)
+// Matrix-core path (16-bit or FP8 caches, block_size 16 x 2^k)
 //   Scores: S^T[token][g] = K[token][:] . Q[g][:] with v_mfma_f32_16x16x32
 //   (bf16 or f16): K is the A operand and is loaded straight from HBM in the
 //   operand layout (lane = token, 16-byte chunks of the row), Q (padded to 16
@@ -38,14 +38,14 @@
 //   lane%16 in lane `lane`, which is exactly the B-operand layout the PV
 //   product needs, so probabilities never move between lanes.
 //   PV: O^T[d][g] += V^T[d][token] P^T[token][g].  The contraction index is
-//   the token, so V must be transposed: each lane loads 4 token rows of an
-//   8-element d-chunk with coalesced 16-byte loads, packs the 4 tokens of each
-//   d into 8 bytes and stores them into a per-wave LDS tile [d][token]
-//   (rows XOR-swizzled to spread banks); the MFMA A operand is then one
-//   8-byte LDS read per 16-row output tile.  The probabilities are split into
-//   a hi and a lo 16-bit part (p = hi + lo + O(2^-16 p)) carried in the upper
-//   and lower halves of the MFMA's K = 32 (V is duplicated in the A operand),
-//   so one instruction applies both and P keeps ~16 bits of precision.
+//   the token, so the A operand is V transposed: each wave stores its tile's
+//   V rows, as loaded (4 token rows of a d-chunk per 16-byte load), into a
+//   per-wave LDS tile in their natural [token][d] layout (16-byte chunks
+//   XOR-swizzled by the row to spread banks), and one transposing LDS read
+//   (ds_read_b64_tr_b16) per 16 rows of d returns the 4 tokens x 1 d cell
+//   each lane needs.  The probabilities are split into a hi and a lo 16-bit
+//   part (p = hi + lo + O(2^-16 p)) and applied by two v_mfma_f32_16x16x16
+//   per 16 rows of d, so P keeps ~16 bits of precision.
 //   FP8 (OCP E4M3) K/V are converted in registers by the hardware converter
 //   (exact into bf16/f16); k_scale folds into the logit scale and v_scale
 //   into the final normalisation.
@@ -61,6 +61,17 @@
 //   atomic stores and loads, which the gfx950 memory system keeps coherent
 //   across the XCDs' separate L2 caches without writing back or invalidating
 //   whole caches; a vmcnt(0) wait orders them before the counter increment.
+//
+// Several new query tokens per sequence (MT)
+//   The 16 MFMA columns hold (query token, query head) rows of a 16-row tile
+//   instead of the group's heads; each lane masks scores past its row's
+//   causal limit, and the row tiles of one (sequence, KV head) run on one XCD
+//   so that their walks of its K/V share that XCD's L2.
+//
+// Decode step (AP): the new tokens' scatter inside the launch
+//   The one wave that reads a sequence's last position writes the new token
+//   there, and computes that tile with the rows it wrote (staged in LDS)
+//   instead of the loaded ones, so nothing waits for the write.
 //
 // Vector path (fp32 caches, any block size): the same decomposition, one
 // token at a time, lanes owning head dimensions, fp32 FMAs and wave
