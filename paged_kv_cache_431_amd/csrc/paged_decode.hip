@@ -402,6 +402,14 @@ struct MfmaTile {
   static constexpr int ES = KV == kFP8 ? 1 : 2;  // bytes per cached element
   static constexpr int ROW = D * ES;              // bytes of one token's row (one head)
   static constexpr int KCH = ROW / 64;            // 16-byte K chunks per lane
+  // K is loaded 1 KiB at a time (lane l: bytes 16 l .. 16 l + 15 of the
+  // tile's 1 KiB piece c, so every load covers whole cache lines); the rows go
+  // to a per-wave LDS tile and come back in the MFMA operand layout.  LDS rows
+  // are padded by 16 bytes (KLDS = ROW + 16): the 16 rows an operand read
+  // touches then fall on different banks for ROW = 64, 128 and 256.
+  static constexpr int LPR = ROW / 16;  // 16-byte chunks (lanes) per row
+  static constexpr int RPK = 64 / LPR;  // rows per 1 KiB load
+  static constexpr int KLDS = ROW + 16; // LDS bytes per K row
   static constexpr int VB = D * ES / 16;          // V bytes per lane per token row
   static constexpr int VDW = VB / 4;              // ... in dwords (1, 2 or 4)
   // Bytes of K and V one 16-token tile brings in.
@@ -436,6 +444,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       // decode step: the new token's K and V rows as stored in the pools, one
       // copy per wave (each wave stages its own: no barrier)
       uint8_t newrow[kDecodeWaves][2][ROW];
+      // per-wave K tile: row t, 16-byte chunk c at byte t * KLDS + 16 c
+      u32x4 ktile[kDecodeWaves][kTileTokens * Tile::KLDS / 16];
     } t;
     MergeSmem<D> merge;
   } sm;
@@ -557,7 +567,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int32_t* bt_row = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
   const size_t head_bytes = (size_t)p.block_size * ROW;
   const size_t block_bytes = head_bytes * p.h_kv;
-  const uint8_t* kbase = p.k_cache + it.kvh * head_bytes + lo16 * ROW + q4 * 16;
+  const uint8_t* kbase = p.k_cache + it.kvh * head_bytes + lane * 16;
   const uint8_t* vbase = p.v_cache + it.kvh * head_bytes + (4 * q4) * ROW + lo16 * Tile::VB;
 
   // Decode step: the wave whose tiles include the sequence's last position
@@ -571,12 +581,19 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
 
   auto compute_tile = [&](Tile& r, bool valid) {
     const int lim = valid ? r.lim : 0;
+    // 0) K rows into the wave's LDS tile (lane l of load c holds chunk
+    //    l % LPR of row RPK c + l / LPR)
+    uint8_t* kt = reinterpret_cast<uint8_t*>(sm.t.ktile[wave]);
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+      *reinterpret_cast<u32x4*>(kt + (Tile::RPK * c + lane / Tile::LPR) * Tile::KLDS + (lane % Tile::LPR) * 16) =
+          r.k[c];
     if constexpr (AP) {
       if (owner && valid && r.tok0 == last_tok0) {  // the tile holding the new token (wave-uniform)
         const int row = it.ctx - 1 - r.tok0;
-        if (lo16 == row) {
-#pragma unroll
-          for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(&sm.t.newrow[wave][0][q4 * 16 + c * 64]);
+        if (lane < Tile::LPR) {
+          *reinterpret_cast<u32x4*>(kt + row * Tile::KLDS + lane * 16) =
+              *reinterpret_cast<const u32x4*>(&sm.t.newrow[wave][0][lane * 16]);
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -588,17 +605,21 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         }
       }
     }
+    // K in the operand layout: lane (lo16, q4) holds chunk q4 + 4 c of row lo16
+    u32x4 kr[KCH];
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) kr[c] = *reinterpret_cast<const u32x4*>(kt + lo16 * Tile::KLDS + (q4 + 4 * c) * 16);
     // 1) scores for the 16 tokens of the tile against the (padded) query group
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       u32x4 a;
       if constexpr (KV == kFP8) {
-        const uint32_t w0 = r.k[kk >> 1][2 * (kk & 1)], w1 = r.k[kk >> 1][2 * (kk & 1) + 1];
+        const uint32_t w0 = kr[kk >> 1][2 * (kk & 1)], w1 = kr[kk >> 1][2 * (kk & 1) + 1];
         a = u32x4{fp8x2_to_pair<CT, false>(w0), fp8x2_to_pair<CT, true>(w0), fp8x2_to_pair<CT, false>(w1),
                   fp8x2_to_pair<CT, true>(w1)};
       } else {
-        a = r.k[kk];
+        a = kr[kk];
       }
       sc = mfma_16x16x32<CT>(a, qop[kk], sc);
     }
@@ -745,7 +766,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
       const uint8_t* kp = kbase + off;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kp + c * 64);
+      for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kp + c * 1024);
       const uint8_t* vp = vbase + off;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
