@@ -53,9 +53,9 @@ MULTI_TOKENS = 4
 
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("a83c03b34497eae8224cb4a9cea3d917f29313352d3ce6fc711b8bf21db3c561", "gqa70b-bf16-47x825-step", 1): 163106762,
-    ("a83c03b34497eae8224cb4a9cea3d917f29313352d3ce6fc711b8bf21db3c561", "gqa70b-bf16-47x825", 1): 162696112,
-    ("a83c03b34497eae8224cb4a9cea3d917f29313352d3ce6fc711b8bf21db3c561", "gqa70b-bf16-47x825-multi4", 1): 171601947,
+    ("28969dd051b2cf97b86fd2586fc7545ae106bac1106bbb6a3599008a27baf3d6", "gqa70b-bf16-47x825-step", 1): 163105179,
+    ("28969dd051b2cf97b86fd2586fc7545ae106bac1106bbb6a3599008a27baf3d6", "gqa70b-bf16-47x825", 1): 162708506,
+    ("28969dd051b2cf97b86fd2586fc7545ae106bac1106bbb6a3599008a27baf3d6", "gqa70b-bf16-47x825-multi4", 1): 172572139,
 }
 
 
