@@ -20,8 +20,13 @@ host memory and back in one launch each way, GB/s against PCIe 5.0 x16.
 multi_query = a speculative step: 4 new query tokens per sequence (the last 4
 positions of each context, causal), the same pools; GB/s counts each cached
 K/V byte once.
+reshape_and_cache = the separate scatter's launch time (reported, not a
+target); bytes_per_layer_call = the bytes a call moves besides the used K/V
+(whole blocks, queries, output, tables, new tokens), not counted in value.
+roofline.measured_stream_peaks = a 2 GiB device copy's read + write rate and
+a 2 GiB float32 sum's read rate (library kernels), beside the published 8 TB/s.
 cpu_baseline = the float64 oracle on whole layer calls, repeated for a
-bounded time on the host.
+bounded time on the host, with all its threads and then with one.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
 """
@@ -93,10 +98,68 @@ def kv_bytes_per_call(plan, unique=True):
     return total
 
 
-def cpu_baseline(plan, rp, tensors, budget_s):
+def side_bytes_per_call(plan, fused):
+    """Bytes a layer call moves besides the used K/V tokens, reported beside
+    the headline figure but not counted in it: the whole blocks the used
+    tokens lie in (the tail slots of each last block are fetched with it),
+    the per-sequence bytes the shared prefix blocks would take if every
+    sequence had its own copy, the queries, the output, the block tables and
+    context lengths, and the new tokens' K/V."""
+    import workloads
+    wl = plan.workload
+    e_kv = workloads.ELEMENT_BYTES[wl.kv_dtype]
+    per_token = 2 * wl.h_kv * wl.head_dim * e_kv
+    ctx = plan.context_lens.astype("int64")
+    blocks = -(-ctx // wl.block_size)
+    allocated = int(blocks.sum()) * wl.block_size * per_token
+    if wl.layout == "shared_prefix":
+        groups = -(-wl.num_seqs // wl.group_size)
+        allocated -= (wl.num_seqs - groups) * wl.prefix_tokens * per_token
+    new_tok = wl.num_seqs * 2 * wl.h_kv * wl.head_dim
+    return {
+        "kv_used_bytes": kv_bytes_per_call(plan),
+        "kv_logical_bytes": kv_bytes_per_call(plan, unique=False),
+        "kv_allocated_bytes": allocated,
+        "q_bytes": wl.num_seqs * wl.h_q * wl.head_dim * workloads.ELEMENT_BYTES[wl.q_dtype],
+        "out_bytes": wl.num_seqs * wl.h_q * wl.head_dim * 4,
+        "block_table_bytes": int(sum(int(b) for b in blocks)) * 4,
+        "context_len_bytes": wl.num_seqs * 4,
+        "new_kv_read_bytes": new_tok * workloads.ELEMENT_BYTES[wl.new_dtype] if fused else 0,
+        "new_kv_written_bytes": new_tok * e_kv if fused else 0,
+    }
+
+
+def stream_peaks(dev, nbytes, reps=10):
+    """Streaming rates the memory system gives plain library kernels on
+    nbytes: a device-to-device copy (the runtime's copy kernel; read + write
+    bytes) and a float32 sum (torch's reduction; bytes read), GB/s."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+
+    def median_ms(fn):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+
+    copy_ms = median_ms(lambda: dst.copy_(src))
+    sum_ms = median_ms(lambda: torch.sum(src))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (copy_ms * 1e-3) / 1e9, nbytes / (sum_ms * 1e-3) / 1e9
+
+
+def cpu_baseline(plan, rp, tensors, budget_s, one_thread_budget_s):
     """Time the oracle on whole layer calls of the workload (the scatter of the
     new tokens, then float64 attention one sequence at a time), repeating the
-    layer until about budget_s seconds of host work are done."""
+    layer until about budget_s seconds of host work are done; then the same
+    with every thread pool held to one thread for one_thread_budget_s."""
     import numpy as np
     import torch
 
@@ -110,32 +173,52 @@ def cpu_baseline(plan, rp, tensors, budget_s):
     q, kc, vc = to_np(tensors.q), to_np(tensors.k_cache), to_np(tensors.v_cache)
     nk, nv = to_np(tensors.new_k), to_np(tensors.new_v)
     per_call = kv_bytes_per_call(plan)
-    done_calls, done_seqs, done_bytes = 0, 0, 0
-    t0 = time.perf_counter()
-    while True:
-        kc2, vc2 = oracle.scatter.reshape_and_cache(nk, nv, kc, vc, rp.slot_mapping, in_dtype=wl.new_dtype,
-                                                    kv_dtype=wl.kv_dtype, block_size=wl.block_size,
-                                                    k_scale=tensors.k_scale, v_scale=tensors.v_scale)
-        for s in range(wl.num_seqs):
-            oracle.attention.paged_attention_decode(q, kc2, vc2, rp.block_tables, plan.context_lens,
-                                                    q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype,
-                                                    block_size=wl.block_size, scale=1.0 / math.sqrt(wl.head_dim),
-                                                    k_scale=tensors.k_scale, v_scale=tensors.v_scale, seqs=[s])
-        done_calls += 1
-        done_seqs += wl.num_seqs
-        done_bytes += per_call
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "seqs_per_s": round(done_seqs / dt, 3), "host_cpus": os.cpu_count(),
-            "sample": f"{done_calls} repeats of one layer call of {wl.name} ({wl.num_seqs} sequences: scatter of the "
-                      f"new tokens, then float64 attention one sequence at a time), {dt:.1f} s"}
+
+    def run(budget):
+        done_calls = 0
+        t0 = time.perf_counter()
+        while True:
+            kc2, vc2 = oracle.scatter.reshape_and_cache(nk, nv, kc, vc, rp.slot_mapping, in_dtype=wl.new_dtype,
+                                                        kv_dtype=wl.kv_dtype, block_size=wl.block_size,
+                                                        k_scale=tensors.k_scale, v_scale=tensors.v_scale)
+            for s in range(wl.num_seqs):
+                oracle.attention.paged_attention_decode(q, kc2, vc2, rp.block_tables, plan.context_lens,
+                                                        q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype,
+                                                        block_size=wl.block_size,
+                                                        scale=1.0 / math.sqrt(wl.head_dim),
+                                                        k_scale=tensors.k_scale, v_scale=tensors.v_scale, seqs=[s])
+            done_calls += 1
+            if time.perf_counter() - t0 > budget:
+                return done_calls, time.perf_counter() - t0
+
+    def threads_in_use():
+        try:
+            from threadpoolctl import threadpool_info
+            return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+        except Exception:
+            return 1
+
+    def sample(calls, dt):
+        return (f"{calls} repeats of one layer call of {wl.name} ({wl.num_seqs} sequences: scatter of the new "
+                f"tokens, then float64 attention one sequence at a time), {dt:.1f} s")
+
+    calls, dt = run(budget_s)
+    result = {"value": round(calls * per_call / dt / 1e9, 4), "unit": "GB/s", "cores": threads_in_use(),
+              "kind": "oracle", "seqs_per_s": round(calls * wl.num_seqs / dt, 3), "host_cpus": os.cpu_count(),
+              "sample": sample(calls, dt)}
+    if one_thread_budget_s > 0:
+        from threadpoolctl import threadpool_limits
+        torch_threads = torch.get_num_threads()
+        with threadpool_limits(limits=1):
+            torch.set_num_threads(1)
+            try:
+                calls1, dt1 = run(one_thread_budget_s)
+                cores1 = threads_in_use()
+            finally:
+                torch.set_num_threads(torch_threads)
+        result["one_thread"] = {"value": round(calls1 * per_call / dt1 / 1e9, 4), "unit": "GB/s", "cores": cores1,
+                                "seqs_per_s": round(calls1 * wl.num_seqs / dt1, 3), "sample": sample(calls1, dt1)}
+    return result
 
 
 def swap_measurement(pkv, t, plan, wl, stream, n_pairs, _hbm_peak):
@@ -191,6 +274,10 @@ def main():
     ap.add_argument("--block-size", type=int, default=0, help="tokens per block (0: the workload's own, 16)")
     ap.add_argument("--splits", type=int, default=0, help="force the decode split count (0 = library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget-one-thread", type=float, default=10.0,
+                    help="seconds of oracle work held to one thread (0 skips that run)")
+    ap.add_argument("--copy-peak-mib", type=int, default=2048,
+                    help="buffer size of the copy and sum that measure streaming rates (0 skips them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB a few times (calibrates byte counters), then exit")
@@ -313,6 +400,24 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         decode_only_ms = sum(a.elapsed_time(b) for a, b in batch) / (reps * L)
+    # reshape_and_cache alone over the same pools (launch-bound: reported, not a target)
+    batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in batch:
+        a.record(stream)
+        for call in scatters:
+            call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    scatter_ms = sum(a.elapsed_time(b) for a, b in batch) / (reps * L)
+    sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+    for (a, b), call in zip(sevs, scatters):
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    scatter_iso = sorted(a.elapsed_time(b) for a, b in sevs)
+    pct = lambda xs, f: xs[min(len(xs) - 1, int(f * len(xs)))]
+    peaks = stream_peaks(dev, args.copy_peak_mib << 20) if args.copy_peak_mib else None
 
     per_call = kv_bytes_per_call(plan)
     step_bytes = per_call * L
@@ -350,6 +455,15 @@ def main():
                                 "decode_mfma_kernel" if wl.kv_dtype != "f32" else "decode_vector_kernel"),
                      "mean_launch_us": round(mean_launch_ms * 1e3, 3),
                      "isolated_launch_median_us": round(launch_ms[len(launch_ms) // 2] * 1e3, 3),
+                     "isolated_launch_p10_us": round(pct(launch_ms, 0.1) * 1e3, 3),
+                     "isolated_launch_p90_us": round(pct(launch_ms, 0.9) * 1e3, 3),
+                     "isolated_launches": len(launch_ms),
+                     "measured_stream_peaks": (None if peaks is None else
+                                               {"copy_GBps": round(peaks[0], 1), "sum_GBps": round(peaks[1], 1),
+                                                "buffer_bytes": args.copy_peak_mib << 20,
+                                                "note": "device-to-device copy (read + write bytes) and float32 "
+                                                        "sum (bytes read) of one buffer, median of 10",
+                                                "achieved_over_sum": round(achieved / peaks[1], 4)}),
                      "algorithmic_bytes_per_launch": per_call,
                      "decode_only_mean_launch_us": round(decode_only_ms * 1e3, 3)},
     }
@@ -369,6 +483,12 @@ def main():
     copy_ms = a.elapsed_time(b) / 10
     block_bytes = wl.h_kv * wl.block_size * wl.head_dim * workloads.ELEMENT_BYTES[wl.kv_dtype]
     moved = n_pairs * 2 * block_bytes * 2  # K and V blocks, each read once and written once
+    result["bytes_per_layer_call"] = side_bytes_per_call(plan, fused)
+    result["reshape_and_cache"] = {"mean_launch_us": round(scatter_ms * 1e3, 3),
+                                   "isolated_launch_median_us": round(scatter_iso[len(scatter_iso) // 2] * 1e3, 3),
+                                   "new_tokens": wl.num_seqs,
+                                   "note": "the two-launch path's scatter alone; the decode step writes the new "
+                                           "tokens inside its attention kernel"}
     result["copy_blocks"] = {"pairs": n_pairs, "block_bytes_per_pool": block_bytes, "us_per_call": round(copy_ms * 1e3, 3),
                              "read_plus_write_GBps": round(moved / (copy_ms * 1e-3) / 1e9, 1),
                              "frac_of_hbm_peak": round(moved / (copy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -408,7 +528,7 @@ def main():
         del pools, decodes, scatters, layer_calls, multis, steps_fused, two_launch_calls, kernel_calls
         torch.cuda.empty_cache()
         fresh = workloads.make_tensors(plan, rp, device=dev, poison=False, pool_seed_offset=0)  # untouched by HIP
-        result["cpu_baseline"] = cpu_baseline(plan, rp, fresh, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(plan, rp, fresh, args.cpu_budget, args.cpu_budget_one_thread)
     print(json.dumps(result), flush=True)
 
 
