@@ -27,13 +27,17 @@
 //   flight.  Loads are issued unconditionally (a step past the end re-reads
 //   the wave's last tile, which the L2 serves, and computes nothing), so the
 //   compiler can wait for exactly the oldest tile instead of draining every
-//   outstanding load.
+//   outstanding load.  Decode's K/V loads are non-temporal: nothing re-reads
+//   them, and keeping them out of the caches' normal policy measured 4-9 %
+//   faster.
 //
 // Matrix-core path (16-bit or FP8 caches, block_size 16 x 2^k)
 //   Scores: S^T[token][g] = K[token][:] . Q[g][:] with v_mfma_f32_16x16x32
-//   (bf16 or f16): K is the A operand and is loaded straight from HBM in the
-//   operand layout (lane = token, 16-byte chunks of the row), Q (padded to 16
-//   rows) is the B operand and stays in registers for the whole walk.  The
+//   (bf16 or f16): K is the A operand.  Each K load reads 1 KiB of the tile
+//   contiguously (whole cache lines); the rows pass through a per-wave LDS
+//   tile with rows padded by 16 bytes and come back in the operand layout
+//   (lane = token, 16-byte chunks of the row).  Q (padded to 16 rows) is the
+//   B operand and stays in registers for the whole walk.  The
 //   accumulator layout puts scores for tokens 4*(lane/16)+r of query row
 //   lane%16 in lane `lane`, which is exactly the B-operand layout the PV
 //   product needs, so probabilities never move between lanes.
@@ -394,6 +398,20 @@ __device__ __forceinline__ uint32_t fp8x2_to_pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   } else {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+}
+
+// A K/V load.  Decode reads every cached byte once, so its loads are
+// non-temporal (the caches do not keep the lines for a reuse that never comes:
+// 9 % faster on the 70B-shaped workload); with several query tokens the row
+// tiles of one (sequence, KV head) read the same K/V through one L2, so those
+// loads keep the normal policy.
+template <bool STREAM, class T>
+__device__ __forceinline__ T kv_load(const uint8_t* p) {
+  if constexpr (STREAM) {
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  } else {
+    return *reinterpret_cast<const T*>(p);
   }
 }
 
@@ -766,22 +784,22 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
       const uint8_t* kp = kbase + off;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kp + c * 1024);
+      for (int c = 0; c < KCH; ++c) r.k[c] = kv_load<!MT, u32x4>(kp + c * 1024);
       const uint8_t* vp = vbase + off;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         if constexpr (VDW == 4) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(vp + rr * ROW);
+          const u32x4 x = kv_load<!MT, u32x4>(vp + rr * ROW);
           r.v[rr][0] = x[0];
           r.v[rr][1] = x[1];
           r.v[rr][2] = x[2];
           r.v[rr][3] = x[3];
         } else if constexpr (VDW == 2) {
-          const u32x2 x = *reinterpret_cast<const u32x2*>(vp + rr * ROW);
+          const u32x2 x = kv_load<!MT, u32x2>(vp + rr * ROW);
           r.v[rr][0] = x[0];
           r.v[rr][1] = x[1];
         } else {
-          r.v[rr][0] = *reinterpret_cast<const uint32_t*>(vp + rr * ROW);
+          r.v[rr][0] = kv_load<!MT, uint32_t>(vp + rr * ROW);
         }
       }
     };
