@@ -24,12 +24,13 @@
 //   A wave first loads the physical block ids of up to 64 of its tiles, one
 //   per lane, then streams the tiles through a ring of NBUF register buffers:
 //   while tile i is computed, the loads of the next NBUF-1 tiles are in
-//   flight.  Loads are issued unconditionally (a step past the end re-reads
-//   the wave's last tile, which the L2 serves, and computes nothing), so the
-//   compiler can wait for exactly the oldest tile instead of draining every
-//   outstanding load.  Decode's K/V loads are non-temporal: nothing re-reads
-//   them, and keeping them out of the caches' normal policy measured 4-9 %
-//   faster.
+//   flight.  Loads are issued unconditionally, so the compiler can wait for
+//   exactly the oldest tile instead of draining every outstanding load.  With
+//   16-bit caches each tile's loads go through a buffer resource sized to the
+//   tile, and a ring step past the wave's last tile gets a resource of size
+//   0, whose loads return zeros without a memory access; with FP8 caches such
+//   a step re-reads the last tile.  Either way it computes nothing.  Decode's
+//   K/V loads are non-temporal: nothing re-reads them.
 //
 // Matrix-core path (16-bit or FP8 caches, block_size 16 x 2^k)
 //   Scores: S^T[token][g] = K[token][:] . Q[g][:] with v_mfma_f32_16x16x32
@@ -401,18 +402,36 @@ __device__ __forceinline__ uint32_t fp8x2_to_pair(uint32_t w) {
   }
 }
 
-// A K/V load.  Decode reads every cached byte once, so its loads are
-// non-temporal (the caches do not keep the lines for a reuse that never comes:
-// 9 % faster on the 70B-shaped workload); with several query tokens the row
-// tiles of one (sequence, KV head) read the same K/V through one L2, so those
-// loads keep the normal policy.
+// 16-bit K/V loads go through a buffer resource per tile: its base is the
+// tile's address (wave-uniform), its size the tile's bytes, or 0 for a ring
+// step past the wave's last tile or a block id outside the pool, whose loads
+// then return zeros without touching memory (the hardware's range check), so
+// the ring issues every load unconditionally and reads no byte twice.  FP8
+// tiles (half the bytes, so twice the tiles per byte) measured faster with
+// plain loads, a step past the end re-reading the last tile.  Decode reads
+// every cached byte once, so its loads are non-temporal (the caches do not
+// keep the lines for a reuse that never comes); with several query tokens the
+// row tiles of one (sequence, KV head) read the same K/V through one L2, so
+// those loads keep the normal policy.  In a buffer load the per-lane part of
+// the offset is a vector register, the part common to the wave a scalar one.
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) 32-bit data format
+
 template <bool STREAM, class T>
-__device__ __forceinline__ T kv_load(const uint8_t* p) {
+__device__ __forceinline__ T kv_gload(const uint8_t* p) {
   if constexpr (STREAM) {
     return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
   } else {
     return *reinterpret_cast<const T*>(p);
   }
+}
+
+template <bool STREAM>
+__device__ __forceinline__ u32x4 kv_load16(__amdgpu_buffer_rsrc_t r, int lane_off, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, STREAM ? 2 : 0));
+}
+template <bool STREAM>
+__device__ __forceinline__ u32x2 kv_load8(__amdgpu_buffer_rsrc_t r, int lane_off, int off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, off, STREAM ? 2 : 0));
 }
 
 template <int KV, int D>
@@ -585,8 +604,10 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int32_t* bt_row = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
   const size_t head_bytes = (size_t)p.block_size * ROW;
   const size_t block_bytes = head_bytes * p.h_kv;
-  const uint8_t* kbase = p.k_cache + it.kvh * head_bytes + lane * 16;
-  const uint8_t* vbase = p.v_cache + it.kvh * head_bytes + (4 * q4) * ROW + lo16 * Tile::VB;
+  const uint8_t* k_head = p.k_cache + it.kvh * head_bytes;
+  const uint8_t* v_head = p.v_cache + it.kvh * head_bytes;
+  const int k_lane = lane * 16;                           // K: 16 bytes of each 1 KiB piece
+  const int v_lane = (4 * q4) * ROW + lo16 * Tile::VB;    // V: row 4 q4 + rr, chunk lo16
 
   // Decode step: the wave whose tiles include the sequence's last position
   // (the last tile of the last split) appends the new token: it computes
@@ -772,7 +793,10 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       if (c0 == 0 && owner) stage_new_token();
     }
 
-    auto load_tile = [&](Tile& r, int j) {  // j: tile of the chunk, 0 <= j < cn (wave-uniform)
+    // jr: the ring step's tile of the chunk (wave-uniform); jr >= cn past the
+    // end, where the loads return zeros without a memory access
+    auto load_tile = [&](Tile& r, int jr) {
+      const int j = min(jr, cn - 1);
       const int tok0 = (t0 + j) * kTileTokens;
       int phys = __builtin_amdgcn_readlane(ids, j);
       const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
@@ -782,24 +806,42 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       r.tok0 = tok0;
       const int sub = (t0 + j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
       const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
-      const uint8_t* kp = kbase + off;
+      if constexpr (KV != kFP8) {
+        const int bytes = ok && jr < cn ? kTileTokens * ROW : 0;
+        const __amdgpu_buffer_rsrc_t kr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k_head + off), (short)0, bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t vr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(v_head + off), (short)0, bytes, kBufferWord3);
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) r.k[c] = kv_load<!MT, u32x4>(kp + c * 1024);
-      const uint8_t* vp = vbase + off;
+        for (int c = 0; c < KCH; ++c) r.k[c] = kv_load16<!MT>(kr, k_lane, c * 1024);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        if constexpr (VDW == 4) {
-          const u32x4 x = kv_load<!MT, u32x4>(vp + rr * ROW);
-          r.v[rr][0] = x[0];
-          r.v[rr][1] = x[1];
-          r.v[rr][2] = x[2];
-          r.v[rr][3] = x[3];
-        } else if constexpr (VDW == 2) {
-          const u32x2 x = kv_load<!MT, u32x2>(vp + rr * ROW);
-          r.v[rr][0] = x[0];
-          r.v[rr][1] = x[1];
-        } else {
-          r.v[rr][0] = kv_load<!MT, uint32_t>(vp + rr * ROW);
+        for (int rr = 0; rr < 4; ++rr) {
+          if constexpr (VDW == 4) {
+            const u32x4 x = kv_load16<!MT>(vr, v_lane, rr * ROW);
+            r.v[rr][0] = x[0];
+            r.v[rr][1] = x[1];
+            r.v[rr][2] = x[2];
+            r.v[rr][3] = x[3];
+          } else {
+            const u32x2 x = kv_load8<!MT>(vr, v_lane, rr * ROW);
+            r.v[rr][0] = x[0];
+            r.v[rr][1] = x[1];
+          }
+        }
+      } else {
+        const uint8_t* kp = k_head + off + k_lane;
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) r.k[c] = kv_gload<!MT, u32x4>(kp + c * 1024);
+        const uint8_t* vp = v_head + off + v_lane;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          if constexpr (VDW == 2) {
+            const u32x2 x = kv_gload<!MT, u32x2>(vp + rr * ROW);
+            r.v[rr][0] = x[0];
+            r.v[rr][1] = x[1];
+          } else {
+            r.v[rr][0] = kv_gload<!MT, uint32_t>(vp + rr * ROW);
+          }
         }
       }
     };
@@ -808,7 +850,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     Tile buf[NBUF];
 #pragma unroll
     for (int b = 0; b < NBUF - 1; ++b) {
-      load_tile(buf[b], min(b, cn - 1));
+      load_tile(buf[b], b);
       // keep the tiles' loads in ring order, so that waiting for the oldest
       // tile never waits for a younger one
       __builtin_amdgcn_sched_barrier(0);
@@ -819,7 +861,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     for (int i = 0; i < cn; i += NBUF) {
 #pragma unroll
       for (int b = 0; b < NBUF; ++b) {
-        load_tile(buf[(b + NBUF - 1) % NBUF], min(i + b + NBUF - 1, cn - 1));
+        load_tile(buf[(b + NBUF - 1) % NBUF], i + b + NBUF - 1);
         compute_tile(buf[b], i + b < cn);
       }
     }
