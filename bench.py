@@ -46,21 +46,21 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "gqa70b-bf16-47x825"
 
 
-# HBM bytes per launch from rocprofv3 counters (FETCH_SIZE x 2 + WRITE_SIZE:
-# on a 1 GiB device copy FETCH_SIZE reads half the bytes read and WRITE_SIZE
-# all the bytes written), valid only for the kernel code they were taken on
-# (kernel_source_sha256) and the workload / split count they ran.
 # Host link of an MI355X: PCIe 5.0 x16, per direction.
 PCIE_PEAK_GBS = 64.0
 
 # Lookahead tokens per sequence of the speculative step measured beside decode.
 MULTI_TOKENS = 4
 
+# HBM bytes per launch from rocprofv3 counters (FETCH_SIZE x 2 + WRITE_SIZE:
+# on a 1 GiB device copy FETCH_SIZE reads half the bytes read and WRITE_SIZE
+# all the bytes written), valid only for the kernel code they were taken on
+# (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("28969dd051b2cf97b86fd2586fc7545ae106bac1106bbb6a3599008a27baf3d6", "gqa70b-bf16-47x825-step", 1): 163105179,
-    ("28969dd051b2cf97b86fd2586fc7545ae106bac1106bbb6a3599008a27baf3d6", "gqa70b-bf16-47x825", 1): 162708506,
-    ("28969dd051b2cf97b86fd2586fc7545ae106bac1106bbb6a3599008a27baf3d6", "gqa70b-bf16-47x825-multi4", 1): 172572139,
+    ("345108dad911761128dfcf161b4c637c953ca6001ef339ca34636a43b56e0035", "gqa70b-bf16-47x825-step", 1): 163103245,
+    ("345108dad911761128dfcf161b4c637c953ca6001ef339ca34636a43b56e0035", "gqa70b-bf16-47x825", 1): 162721792,
+    ("345108dad911761128dfcf161b4c637c953ca6001ef339ca34636a43b56e0035", "gqa70b-bf16-47x825-multi4", 1): 171791035,
 }
 
 
