@@ -27,14 +27,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kStartCost = 2;
 constexpr int64_t kMergeCost = 6;
 
-int choose_splits(int64_t units, int64_t max_tiles) {
+int choose_splits(int64_t units, int64_t max_tiles, int64_t resident = kResidentWorkgroups) {
   if (max_tiles <= 1 || units <= 0) return 1;
   const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(max_tiles, 8)));
   const int64_t padded_units = ceil_div(units, 8) * 8;
   int best = 1;
   int64_t best_cost = INT64_MAX;
   for (int64_t n = 1; n <= cap; ++n) {
-    const int64_t rounds = ceil_div(padded_units * n, kResidentWorkgroups);
+    const int64_t rounds = ceil_div(padded_units * n, resident);
     const int64_t per_wave = ceil_div(ceil_div(max_tiles, n), pkv::kDecodeWaves);
     const int64_t cost = rounds * (per_wave + kStartCost + (n > 1 ? kMergeCost : 0));
     if (cost < best_cost) {
@@ -91,11 +91,15 @@ bool multi_shape_ok(int num_seqs, int h_q, int h_kv, int head_dim, int block_siz
          max_query_len >= 1 && max_query_len <= kMaxQueryLen;
 }
 
-// Splits for several query tokens: the units are (sequence, KV head, row tile).
+// Splits for several query tokens: the units are (sequence, KV head, row
+// group), a row group being the row tiles one workgroup holds.
 int resolve_multi_splits(int num_seqs, int h_q, int h_kv, int max_query_len, int max_context_len, int num_splits) {
   const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
-  const int64_t units = (int64_t)num_seqs * h_kv * pkv::multi_row_tiles(h_q, h_kv, max_query_len);
-  int n = num_splits > 0 ? num_splits : choose_splits(units, max_tiles);
+  const int row_tiles = pkv::multi_row_tiles(h_q, h_kv, max_query_len);
+  const int64_t units = (int64_t)num_seqs * h_kv * pkv::multi_row_groups(row_tiles);
+  // workgroups holding two row tiles run at 2 waves per SIMD: 2 per CU
+  const int64_t resident = pkv::multi_tiles_per_workgroup(row_tiles) == 2 ? 256 * 2 : kResidentWorkgroups;
+  int n = num_splits > 0 ? num_splits : choose_splits(units, max_tiles, resident);
   return std::max(1, n);
 }
 
@@ -142,7 +146,8 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   const int n = multi ? resolve_multi_splits(num_seqs, h_q, h_kv, max_query_len, max_context_len, num_splits)
                       : resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
   const int row_tiles = multi ? pkv::multi_row_tiles(h_q, h_kv, max_query_len) : 1;
-  if ((int64_t)ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_tiles * n > INT32_MAX) return PKV_EUNSUPPORTED;
+  const int row_groups = multi ? pkv::multi_row_groups(row_tiles) : 1;
+  if ((int64_t)ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_groups * n > INT32_MAX) return PKV_EUNSUPPORTED;
   const pkv::WorkspaceLayout L = multi ? pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n)
                                        : pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n);
   if (workspace_bytes < L.total) return PKV_EWORKSPACE;

@@ -114,7 +114,8 @@ struct Params {
   // sequence s are [query_start[s], query_start[s + 1]) of q and out.
   const int32_t* query_start;
   int num_query_tokens, max_query_len;
-  int row_tiles;  // 16-row tiles of (query token, head) rows per (sequence, KV head)
+  int row_tiles;   // 16-row tiles of (query token, head) rows per (sequence, KV head)
+  int row_groups;  // workgroups per (sequence, KV head, split): row_tiles / RT, rounded up
   // Decode step that appends each sequence's new token itself (null
   // otherwise): new_k, new_v [S, h_kv, D] in new_dtype go to position ctx - 1
   // (its slot from the block table), converted as the scatter converts.
@@ -128,7 +129,7 @@ struct Params {
 
 struct Item {
   int s, kvh, unit, split, ctx, n_tiles, n_splits_seq, t_begin, t_end;
-  int rt, m, q0;  // several query tokens: row tile, query tokens of the sequence, first query row
+  int rt, m, q0;  // several query tokens: first row tile, query tokens of the sequence, first query row
 };
 
 // Workgroup id -> work item.  Consecutive workgroup ids go to the 8 XCDs in
@@ -146,7 +147,7 @@ __device__ __forceinline__ int decode_unit(const Params& p) {
   return ((wg >> 3) / p.num_splits) * 8 + (wg & 7);
 }
 
-template <bool MT>
+template <bool MT, int RT>
 __device__ __forceinline__ bool get_item(const Params& p, Item& it) {
   const int wg = blockIdx.x;
   const int j = wg >> 3;
@@ -156,8 +157,8 @@ __device__ __forceinline__ bool get_item(const Params& p, Item& it) {
   it.rt = 0;
   if constexpr (MT) {
     const int y = it.unit >> 3;
-    it.rt = y % p.row_tiles;
-    base = (y / p.row_tiles) * 8 + (it.unit & 7);
+    it.rt = (y % p.row_groups) * RT;
+    base = (y / p.row_groups) * 8 + (it.unit & 7);
   }
   if (base >= p.units) return false;
   it.s = base / p.h_kv;
@@ -175,8 +176,8 @@ __device__ __forceinline__ bool get_item(const Params& p, Item& it) {
     it.q0 = q0;
     it.m = min(q1 - q0, p.max_query_len);
     const int first_row = it.rt * 16;
-    if (first_row >= it.m * p.group) return false;  // no query row in this tile
-    const int i_last = min(it.m - 1, (first_row + 15) / p.group);
+    if (first_row >= it.m * p.group) return false;  // no query row in these tiles
+    const int i_last = min(it.m - 1, (first_row + 16 * RT - 1) / p.group);
     n_tok = min(ctx, max(0, ctx - it.m + i_last + 1));
   }
   it.n_tiles = (n_tok + kTileTokens - 1) / kTileTokens;
@@ -247,14 +248,14 @@ __device__ __forceinline__ void store_out(const Params& p, size_t row, int chunk
   }
 }
 
-// Output row of row r (0..15) of an item, false if the row holds no query:
-// decode rows are the group's query heads; with several query tokens row
-// r is (query token, head) = divmod(16 * rt + r, group).
+// Output row of row r (0..15) of row tile k of an item, false if the row
+// holds no query: decode rows are the group's query heads; with several query
+// tokens row r of tile k is (query token, head) = divmod(16 (rt + k) + r, group).
 template <bool MT>
-__device__ __forceinline__ bool out_row(const Params& p, const Item& it, int r, size_t& row) {
+__device__ __forceinline__ bool out_row(const Params& p, const Item& it, int k, int r, size_t& row) {
   const int G = p.group;
   if constexpr (MT) {
-    const int gr = it.rt * 16 + r;
+    const int gr = (it.rt + k) * 16 + r;
     const int i = gr / G;
     row = (size_t)(it.q0 + i) * p.h_q + it.kvh * G + (gr - i * G);
     return i < it.m;
@@ -264,30 +265,33 @@ __device__ __forceinline__ bool out_row(const Params& p, const Item& it, int r, 
   }
 }
 
-// Rows that attend over nothing (an empty context) get 0.
+// Rows of row tile k that attend over nothing (an empty context) get 0.
 template <int D, bool MT>
-__device__ void write_zeros(const Params& p, const Item& it) {
+__device__ void write_zeros(const Params& p, const Item& it, int k) {
   constexpr int DW = D / 16;
   const int g = threadIdx.x >> 4, chunk = threadIdx.x & 15;
   size_t row;
-  if (!out_row<MT>(p, it, g, row)) return;
+  if (!out_row<MT>(p, it, k, g, row)) return;
   float z[DW];
 #pragma unroll
   for (int e = 0; e < DW; ++e) z[e] = 0.f;
   store_out<D>(p, row, chunk, z, 1.f);
 }
 
-// Merge the 4 waves' states (already in `sm`, after a barrier), then either
-// write the output (one range) or publish this range's partial state and let
-// the last range of the (sequence, KV head) combine all of them.
-template <int D, bool MT>
-__device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
+// Merge the 4 waves' states of row tile k (already in `sm`, after a
+// barrier), then either write the output (one range) or publish this range's
+// partial state and let the last range of the (sequence, KV head, row tile)
+// combine all of them.  Row tile k of a workgroup of RT row tiles has its
+// own counter and partial rows: index unit * RT + k.
+template <int D, bool MT, int RT>
+__device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm) {
   constexpr int DW = D / 16;
   const int t = threadIdx.x;
   const int g = t >> 4, chunk = t & 15;
-  const int R = MT ? 16 : p.group;  // rows of an item (partial-state rows per split)
+  const int R = MT ? 16 : p.group;  // rows of a row tile (partial-state rows per split)
+  const int cidx = it.unit * RT + k;
   size_t row;
-  const bool row_ok = out_row<MT>(p, it, g, row);
+  const bool row_ok = out_row<MT>(p, it, k, g, row);
   float a[DW];
   float mstar = kNegInf, lstar = 0.f;
 #pragma unroll
@@ -309,7 +313,7 @@ __device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
     if (row_ok) store_out<D>(p, row, chunk, a, lstar > 0.f ? p.v_scale / lstar : 0.f);
     return;
   }
-  const size_t base = (size_t)it.unit * p.num_splits * R + g;  // partial row of split 0
+  const size_t base = (size_t)cidx * p.num_splits * R + g;  // partial row of split 0
   if (row_ok) {
     const size_t prow = base + (size_t)it.split * R;
     float* dst = p.ws_acc + prow * D + chunk * DW;
@@ -323,9 +327,9 @@ __device__ void finish(const Params& p, const Item& it, MergeSmem<D>& sm) {
   wait_vm();  // this range's partial state is complete device-wide before it is counted
   __syncthreads();
   if (t == 0) {
-    const int prev = __hip_atomic_fetch_add(p.counters + it.unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int prev = __hip_atomic_fetch_add(p.counters + cidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == it.n_splits_seq - 1;
-    if (last) __hip_atomic_store(p.counters + it.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) __hip_atomic_store(p.counters + cidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.flag = last;
   }
   __syncthreads();
@@ -408,12 +412,13 @@ __device__ __forceinline__ uint32_t fp8x2_to_pair(uint32_t w) {
 // then return zeros without touching memory (the hardware's range check), so
 // the ring issues every load unconditionally and reads no byte twice.  FP8
 // tiles (half the bytes, so twice the tiles per byte) measured faster with
-// plain loads, a step past the end re-reading the last tile.  Decode reads
-// every cached byte once, so its loads are non-temporal (the caches do not
-// keep the lines for a reuse that never comes); with several query tokens the
-// row tiles of one (sequence, KV head) read the same K/V through one L2, so
-// those loads keep the normal policy.  In a buffer load the per-lane part of
-// the offset is a vector register, the part common to the wave a scalar one.
+// plain loads, a step past the end re-reading the last tile.  When one
+// workgroup is the only reader of a (sequence, KV head)'s K/V, as in decode,
+// the loads are non-temporal (the caches do not keep the lines for a reuse
+// that never comes); when several workgroups (row groups of several query
+// tokens) walk the same K/V, they share it through one L2 and the loads keep
+// the normal policy.  In a buffer load the per-lane part of the offset is a
+// vector register, the part common to the wave a scalar one.
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) 32-bit data format
 
 template <bool STREAM, class T>
@@ -461,9 +466,14 @@ struct MfmaTile {
   int tok0;  // position of its first token
 };
 
-template <int KV, int CT, int D, bool MT, bool AP>
-__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd))) void decode_mfma_kernel(
-    Params p) {
+// RT: 16-row tiles of query rows per workgroup (several query tokens only):
+// with two, one walk of the K/V serves 32 rows, at 2 waves per SIMD for the
+// registers of both tiles' states.  STREAM: K/V loads are non-temporal (the
+// only walk of each (sequence, KV head)); false when several workgroups walk
+// the same K/V and share it through L2.
+template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM>
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(RT == 1 ? kDecodeWavesPerSimd : 2))) void
+decode_mfma_kernel(Params p) {
   using Tile = MfmaTile<KV, D>;
   constexpr int ROW = Tile::ROW;
   constexpr int KCH = Tile::KCH;
@@ -513,9 +523,12 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   }
 
   Item it;
-  if (!get_item<MT>(p, it)) return;
+  if (!get_item<MT, RT>(p, it)) return;
   if (it.n_tiles == 0) {
-    if (it.split == 0) write_zeros<D, MT>(p, it);
+    if (it.split == 0) {
+#pragma unroll
+      for (int k = 0; k < RT; ++k) write_zeros<D, MT>(p, it, k);
+    }
     return;
   }
   if (it.split >= it.n_splits_seq) return;
@@ -528,22 +541,25 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int q4 = lane >> 4;
   const int G = p.group;
 
-  // Q as the B operand: column lo16 is row lo16 of the item (a query head;
-  // with several query tokens a (query token, head) pair), same d order as
-  // the K chunks.  Padding rows hold zeros and never form an address outside
-  // the item's rows.  row_lim: positions [0, row_lim) this row attends to.
-  u32x4 qop[NK];
-  int row_lim = it.ctx;
-  {
+  // Q as the B operand: column lo16 of row tile k is row lo16 of that tile (a
+  // query head; with several query tokens a (query token, head) pair), same
+  // d order as the K chunks.  Padding rows hold zeros and never form an
+  // address outside the item's rows.  row_lim: positions [0, row_lim) the
+  // row attends to.
+  u32x4 qop[RT][NK];
+  int row_lim[RT];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
     bool row_ok;
     size_t qr;
+    row_lim[k] = it.ctx;
     if constexpr (MT) {
-      const int gr = it.rt * 16 + lo16;
+      const int gr = (it.rt + k) * 16 + lo16;
       const int i = gr / G;
       row_ok = i < it.m;
       const int ic = row_ok ? i : it.m - 1;  // it.m >= 1 for an item with rows
       qr = (size_t)(it.q0 + ic) * p.h_q + it.kvh * G + (row_ok ? gr - i * G : 0);
-      row_lim = min(it.ctx, max(0, it.ctx - it.m + ic + 1));
+      row_lim[k] = min(it.ctx, max(0, it.ctx - it.m + ic + 1));
     } else {
       row_ok = lo16 < G;
       qr = (size_t)it.s * p.h_q + it.kvh * G + (row_ok ? lo16 : G - 1);
@@ -552,7 +568,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int d0 = KV == kFP8 ? 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1) : 32 * kk + 8 * q4;
-      qop[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
+      qop[k][kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -590,10 +606,15 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  f32x4 acc[NT];
+  f32x4 acc[RT][NT];
+  float m_run[RT], l_run[RT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int k = 0; k < RT; ++k) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[k][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[k] = kNegInf;
+    l_run[k] = 0.f;
+  }
 
   // This wave's tiles: a contiguous slice [wb, wb + n_my) of the range.
   const int span = it.t_end - it.t_begin;
@@ -648,8 +669,10 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     u32x4 kr[KCH];
 #pragma unroll
     for (int c = 0; c < KCH; ++c) kr[c] = *reinterpret_cast<const u32x4*>(kt + lo16 * Tile::KLDS + (q4 + 4 * c) * 16);
-    // 1) scores for the 16 tokens of the tile against the (padded) query group
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    // 1) scores for the 16 tokens of the tile against each (padded) row tile
+    f32x4 sc[RT];
+#pragma unroll
+    for (int k = 0; k < RT; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       u32x4 a;
@@ -660,7 +683,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       } else {
         a = kr[kk];
       }
-      sc = mfma_16x16x32<CT>(a, qop[kk], sc);
+#pragma unroll
+      for (int k = 0; k < RT; ++k) sc[k] = mfma_16x16x32<CT>(a, qop[k][kk], sc[k]);
     }
     mfma_guard();
 
@@ -700,59 +724,63 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
     compiler_fence();
 
-    // 3) online softmax (log2 domain); row g = lo16, tokens 4*q4 + rr
-    float s[4];
-    // causal limit of this lane's row within the tile (several query tokens)
-    const int row_cut = MT ? min(lim, row_lim - r.tok0) : lim;
+    // 3) online softmax (log2 domain), per row tile; row g = lo16, tokens
+    //    4*q4 + rr; probabilities of those tokens as hi + lo 16-bit parts
+    //    (p = hi + lo + O(2^-16 p)), the B operands of the PV products
+    u32x2 p_hi[RT], p_lo[RT];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      s[rr] = sc[rr] * p.scale_log2;
-      if ((MT || partial) && 4 * q4 + rr >= row_cut) s[rr] = kNegInf;
-    }
-    // Each lane tests its own 4 scores against its row's running max.  Only
-    // when a lane of the wave exceeds it by more than the slack (always for
-    // the first tile with a finite score) are the row maxima formed across
-    // the 4 lanes of each row and the state rescaled; otherwise the tile
-    // needs no cross-lane step at all.
-    const float mx_lane = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    if (__builtin_amdgcn_ballot_w64(mx_lane > m_run + kRescaleSlack) != 0) {
-      float mx = fmaxf(mx_lane, shfl_xor_f32(mx_lane, 16));
-      mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-      const bool grow = mx > m_run + kRescaleSlack;  // the same on the 4 lanes of a row
-      const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run is -inf
-      l_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float pr[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) pr[rr] = fast_exp2(s[rr] - m_use);
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-
-    // probabilities of tokens 4*q4 .. 4*q4+3 as hi + lo 16-bit parts
-    // (p = hi + lo + O(2^-16 p)), the B operands of the PV products
-    u32x2 p_hi, p_lo;
-    if constexpr (CT == kBF16) {
-      float lo_part[4];
-      uint32_t hb[4];
+    for (int k = 0; k < RT; ++k) {
+      float s[4];
+      // causal limit of this lane's row within the tile (several query tokens)
+      const int row_cut = MT ? min(lim, row_lim[k] - r.tok0) : lim;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        hb[rr] = __float_as_uint(pr[rr]) & 0xffff0000u;
-        lo_part[rr] = pr[rr] - __uint_as_float(hb[rr]);
+        s[rr] = sc[k][rr] * p.scale_log2;
+        if ((MT || partial) && 4 * q4 + rr >= row_cut) s[rr] = kNegInf;
       }
-      p_hi = u32x2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u), __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
-      p_lo = u32x2{__builtin_amdgcn_perm(__float_as_uint(lo_part[1]), __float_as_uint(lo_part[0]), 0x07060302u),
-                   __builtin_amdgcn_perm(__float_as_uint(lo_part[3]), __float_as_uint(lo_part[2]), 0x07060302u)};
-    } else {
-      const auto h01 = __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]);
-      const auto h23 = __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]);
-      const auto l01 = __builtin_amdgcn_cvt_pkrtz(pr[0] - (float)h01[0], pr[1] - (float)h01[1]);
-      const auto l23 = __builtin_amdgcn_cvt_pkrtz(pr[2] - (float)h23[0], pr[3] - (float)h23[1]);
-      p_hi = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
-      p_lo = u32x2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+      // Each lane tests its own 4 scores against its row's running max.  Only
+      // when a lane of the wave exceeds it by more than the slack (always for
+      // the first tile with a finite score) are the row maxima formed across
+      // the 4 lanes of each row and the state rescaled; otherwise the tile
+      // needs no cross-lane step at all.
+      const float mx_lane = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      if (__builtin_amdgcn_ballot_w64(mx_lane > m_run[k] + kRescaleSlack) != 0) {
+        float mx = fmaxf(mx_lane, shfl_xor_f32(mx_lane, 16));
+        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+        const bool grow = mx > m_run[k] + kRescaleSlack;  // the same on the 4 lanes of a row
+        const float m_new = grow ? mx : m_run[k];
+        const float alpha = grow ? fast_exp2(m_run[k] - m_new) : 1.f;  // 0 when m_run is -inf
+        l_run[k] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[k][n] *= alpha;
+        m_run[k] = m_new;
+      }
+      const float m_use = m_run[k] == kNegInf ? 0.f : m_run[k];
+      float pr[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) pr[rr] = fast_exp2(s[rr] - m_use);
+      l_run[k] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+      if constexpr (CT == kBF16) {
+        float lo_part[4];
+        uint32_t hb[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          hb[rr] = __float_as_uint(pr[rr]) & 0xffff0000u;
+          lo_part[rr] = pr[rr] - __uint_as_float(hb[rr]);
+        }
+        p_hi[k] = u32x2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                        __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
+        p_lo[k] = u32x2{__builtin_amdgcn_perm(__float_as_uint(lo_part[1]), __float_as_uint(lo_part[0]), 0x07060302u),
+                        __builtin_amdgcn_perm(__float_as_uint(lo_part[3]), __float_as_uint(lo_part[2]), 0x07060302u)};
+      } else {
+        const auto h01 = __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]);
+        const auto h23 = __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]);
+        const auto l01 = __builtin_amdgcn_cvt_pkrtz(pr[0] - (float)h01[0], pr[1] - (float)h01[1]);
+        const auto l23 = __builtin_amdgcn_cvt_pkrtz(pr[2] - (float)h23[0], pr[3] - (float)h23[1]);
+        p_hi[k] = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+        p_lo[k] = u32x2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+      }
     }
 
     // 4) O^T += V^T P^T: per 16 rows of d, two 16x16x16 MFMAs (hi and lo
@@ -774,9 +802,12 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16<CT>(cell[n], p_hi, acc[n]);
+    for (int k = 0; k < RT; ++k) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16<CT>(cell[n], p_lo, acc[n]);
+      for (int n = 0; n < NT; ++n) acc[k][n] = mfma_16x16x16<CT>(cell[n], p_hi[k], acc[k][n]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[k][n] = mfma_16x16x16<CT>(cell[n], p_lo[k], acc[k][n]);
+    }
     mfma_guard();
     compiler_fence();
   };
@@ -813,17 +844,17 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         const __amdgpu_buffer_rsrc_t vr =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(v_head + off), (short)0, bytes, kBufferWord3);
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) r.k[c] = kv_load16<!MT>(kr, k_lane, c * 1024);
+        for (int c = 0; c < KCH; ++c) r.k[c] = kv_load16<STREAM>(kr, k_lane, c * 1024);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           if constexpr (VDW == 4) {
-            const u32x4 x = kv_load16<!MT>(vr, v_lane, rr * ROW);
+            const u32x4 x = kv_load16<STREAM>(vr, v_lane, rr * ROW);
             r.v[rr][0] = x[0];
             r.v[rr][1] = x[1];
             r.v[rr][2] = x[2];
             r.v[rr][3] = x[3];
           } else {
-            const u32x2 x = kv_load8<!MT>(vr, v_lane, rr * ROW);
+            const u32x2 x = kv_load8<STREAM>(vr, v_lane, rr * ROW);
             r.v[rr][0] = x[0];
             r.v[rr][1] = x[1];
           }
@@ -831,16 +862,16 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       } else {
         const uint8_t* kp = k_head + off + k_lane;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) r.k[c] = kv_gload<!MT, u32x4>(kp + c * 1024);
+        for (int c = 0; c < KCH; ++c) r.k[c] = kv_gload<STREAM, u32x4>(kp + c * 1024);
         const uint8_t* vp = v_head + off + v_lane;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           if constexpr (VDW == 2) {
-            const u32x2 x = kv_gload<!MT, u32x2>(vp + rr * ROW);
+            const u32x2 x = kv_gload<STREAM, u32x2>(vp + rr * ROW);
             r.v[rr][0] = x[0];
             r.v[rr][1] = x[1];
           } else {
-            r.v[rr][0] = kv_gload<!MT, uint32_t>(vp + rr * ROW);
+            r.v[rr][0] = kv_gload<STREAM, uint32_t>(vp + rr * ROW);
           }
         }
       }
@@ -885,18 +916,22 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  float l_row = l_run + shfl_xor_f32(l_run, 16);
-  l_row += shfl_xor_f32(l_row, 32);
-
-  __syncthreads();  // every wave is done with its V^T tile: reuse LDS for the merge
 #pragma unroll
-  for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(&sm.merge.acc[wave][lo16][16 * n + 4 * q4]) = acc[n];
-  if (q4 == 0) {
-    sm.merge.m[wave][lo16] = m_run;
-    sm.merge.l[wave][lo16] = l_row;
+  for (int k = 0; k < RT; ++k) {
+    float l_row = l_run[k] + shfl_xor_f32(l_run[k], 16);
+    l_row += shfl_xor_f32(l_row, 32);
+    // every wave is done with its tiles (first row tile) or the previous
+    // row tile's merge has read the LDS: reuse it
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(&sm.merge.acc[wave][lo16][16 * n + 4 * q4]) = acc[k][n];
+    if (q4 == 0) {
+      sm.merge.m[wave][lo16] = m_run[k];
+      sm.merge.l[wave][lo16] = l_row;
+    }
+    __syncthreads();
+    finish<D, MT, RT>(p, it, k, sm.merge);
   }
-  __syncthreads();
-  finish<D, MT>(p, it, sm.merge);
 }
 
 // ---------------------------------------------------------------- vector path
@@ -920,9 +955,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_vector_kernel(Params p)
   __shared__ MergeSmem<D> sm;
 
   Item it;
-  if (!get_item<false>(p, it)) return;
+  if (!get_item<false, 1>(p, it)) return;
   if (it.n_tiles == 0) {
-    if (it.split == 0) write_zeros<D, false>(p, it);
+    if (it.split == 0) write_zeros<D, false>(p, it, 0);
     return;
   }
   if (it.split >= it.n_splits_seq) return;
@@ -991,7 +1026,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_vector_kernel(Params p)
     }
   }
   __syncthreads();
-  finish<D, false>(p, it, sm);
+  finish<D, false, 1>(p, it, 0, sm);
 }
 
 template <typename K>
@@ -1000,12 +1035,16 @@ hipError_t launch(K kernel, int grid, const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool MT, bool AP>
+template <int D, bool MT, bool AP, int RT, bool ST>
 hipError_t dispatch_mfma(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
-  if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP>, grid, p, s);
-  if (a.kv_dtype == kF16 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP>, grid, p, s);
-  if (a.kv_dtype == kFP8 && a.q_dtype == kBF16) return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP>, grid, p, s);
-  if (a.kv_dtype == kFP8 && a.q_dtype == kF16) return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP>, grid, p, s);
+  if (a.kv_dtype == kBF16 && a.q_dtype == kBF16)
+    return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP, RT, ST>, grid, p, s);
+  if (a.kv_dtype == kF16 && a.q_dtype == kF16)
+    return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP, RT, ST>, grid, p, s);
+  if (a.kv_dtype == kFP8 && a.q_dtype == kBF16)
+    return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP, RT, ST>, grid, p, s);
+  if (a.kv_dtype == kFP8 && a.q_dtype == kF16)
+    return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP, RT, ST>, grid, p, s);
   return hipErrorInvalidValue;
 }
 
@@ -1013,14 +1052,21 @@ template <int D>
 hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
   if (a.query_start != nullptr) {
     if (!a.matrix_core || a.new_k != nullptr) return hipErrorInvalidValue;
-    return dispatch_mfma<D, true, false>(a, grid, p, s);
+    // one row group: this workgroup is the K/V's only reader
+    const bool only_reader = p.row_groups == 1;
+    if (multi_tiles_per_workgroup(p.row_tiles) == 2) {
+      return only_reader ? dispatch_mfma<D, true, false, 2, true>(a, grid, p, s)
+                         : dispatch_mfma<D, true, false, 2, false>(a, grid, p, s);
+    }
+    return only_reader ? dispatch_mfma<D, true, false, 1, true>(a, grid, p, s)
+                       : dispatch_mfma<D, true, false, 1, false>(a, grid, p, s);
   }
   if (a.new_k != nullptr) {
     if (!a.matrix_core) return hipErrorInvalidValue;
-    return dispatch_mfma<D, false, true>(a, grid, p, s);
+    return dispatch_mfma<D, false, true, 1, true>(a, grid, p, s);
   }
   if (a.matrix_core) {
-    return dispatch_mfma<D, false, false>(a, grid, p, s);
+    return dispatch_mfma<D, false, false, 1, true>(a, grid, p, s);
   } else {
     if (a.kv_dtype == kF32 && a.q_dtype == kF32) return launch(decode_vector_kernel<kF32, kF32, D>, grid, p, s);
     if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_vector_kernel<kBF16, kBF16, D>, grid, p, s);
@@ -1047,7 +1093,11 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int hea
 
 WorkspaceLayout multi_workspace_layout(int num_seqs, int h_kv, int head_dim, int row_tiles, int num_splits) {
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const size_t units = (((size_t)num_seqs * h_kv + 7) / 8) * 8 * row_tiles;
+  // one counter and 16 partial rows per split for every row tile the
+  // workgroups hold (row groups x tiles per workgroup: one more than
+  // row_tiles when an odd count is held two by two)
+  const size_t units = (((size_t)num_seqs * h_kv + 7) / 8) * 8 * multi_row_groups(row_tiles) *
+                       multi_tiles_per_workgroup(row_tiles);
   const size_t rows = units * num_splits * 16;
   WorkspaceLayout L;
   L.counters = 0;
@@ -1091,6 +1141,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.num_query_tokens = a.num_query_tokens;
   p.max_query_len = a.max_query_len;
   p.row_tiles = row_tiles;
+  p.row_groups = multi ? multi_row_groups(row_tiles) : 1;
   p.new_k = static_cast<const uint8_t*>(a.new_k);
   p.new_v = static_cast<const uint8_t*>(a.new_v);
   p.k_store = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
@@ -1098,7 +1149,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.new_dtype = a.new_dtype;
   p.k_scale_enc = a.k_scale_enc;
   p.v_scale_enc = a.v_scale_enc;
-  const int grid = ((p.units + 7) / 8) * 8 * row_tiles * a.num_splits;
+  const int grid = ((p.units + 7) / 8) * 8 * p.row_groups * a.num_splits;
   if (grid == 0) return hipSuccess;
   if (a.head_dim == 128) return dispatch<128>(a, grid, p, stream);
   if (a.head_dim == 64) return dispatch<64>(a, grid, p, stream);

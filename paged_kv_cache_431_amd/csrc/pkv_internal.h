@@ -55,6 +55,16 @@ inline int multi_row_tiles(int h_q, int h_kv, int max_query_len) {
   return (int)(((int64_t)max_query_len * (h_q / h_kv) + 15) / 16);
 }
 
+// Row tiles one workgroup holds with several query tokens: two (one walk of
+// the K/V for 32 rows) when there are two or more, else one.
+inline int multi_tiles_per_workgroup(int row_tiles) { return row_tiles >= 2 ? 2 : 1; }
+
+// Workgroups per (sequence, KV head, split) with several query tokens.
+inline int multi_row_groups(int row_tiles) {
+  const int t = multi_tiles_per_workgroup(row_tiles);
+  return (row_tiles + t - 1) / t;
+}
+
 // Byte layout of the decode workspace.
 struct WorkspaceLayout {
   size_t counters;  // int32 [units]

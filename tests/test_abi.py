@@ -128,6 +128,9 @@ def test_multi_workspace_and_split_sizing():
     assert pkv.pkv_multi_workspace_bytes(47, 64, 8, 128, 16, 4, 829, 3) >= units * 3 * 16 * (128 + 2) * 4
     assert pkv.pkv_multi_num_splits(47, 64, 8, 128, 16, 4, 829, 3) == 3
     assert pkv.pkv_multi_workspace_bytes(47, 64, 8, 128, 16, 0, 829) == 0
+    # 5 new tokens: 40 rows, 3 row tiles held two per workgroup, so the
+    # workspace has rows for 4 tiles per (sequence, KV head)
+    assert pkv.pkv_multi_workspace_bytes(47, 64, 8, 128, 16, 5, 829, 1) >= 47 * 8 * 4 * 16 * (128 + 2) * 4
     assert pkv.pkv_multi_num_splits(4, 6, 4, 64, 16, 2, 100) == 0
 
 
