@@ -12,7 +12,12 @@
 
 namespace {
 
-constexpr int64_t kResidentWorkgroups = pkv::kResidentDecodeWorkgroups;
+// Workgroups the split model lets run at once: two per CU.  A CU holds
+// three of the decode kernel's, but a third walking K/V beside two slows them
+// more than the smaller ranges gain (32K-token FP8 batch, 256 (sequence, KV
+// head) pairs: 2 splits 261.6 us, 3 splits 277.8 us per launch), and the
+// kernel with two row tiles per workgroup holds two.
+constexpr int64_t kResidentWorkgroups = 256 * 2;
 
 bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
 
@@ -27,14 +32,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kStartCost = 2;
 constexpr int64_t kMergeCost = 6;
 
-int choose_splits(int64_t units, int64_t max_tiles, int64_t resident = kResidentWorkgroups) {
+int choose_splits(int64_t units, int64_t max_tiles) {
   if (max_tiles <= 1 || units <= 0) return 1;
   const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(max_tiles, 8)));
   const int64_t padded_units = ceil_div(units, 8) * 8;
   int best = 1;
   int64_t best_cost = INT64_MAX;
   for (int64_t n = 1; n <= cap; ++n) {
-    const int64_t rounds = ceil_div(padded_units * n, resident);
+    const int64_t rounds = ceil_div(padded_units * n, kResidentWorkgroups);
     const int64_t per_wave = ceil_div(ceil_div(max_tiles, n), pkv::kDecodeWaves);
     const int64_t cost = rounds * (per_wave + kStartCost + (n > 1 ? kMergeCost : 0));
     if (cost < best_cost) {
@@ -97,9 +102,7 @@ int resolve_multi_splits(int num_seqs, int h_q, int h_kv, int max_query_len, int
   const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
   const int row_tiles = pkv::multi_row_tiles(h_q, h_kv, max_query_len);
   const int64_t units = (int64_t)num_seqs * h_kv * pkv::multi_row_groups(row_tiles);
-  // workgroups holding two row tiles run at 2 waves per SIMD: 2 per CU
-  const int64_t resident = pkv::multi_tiles_per_workgroup(row_tiles) == 2 ? 256 * 2 : kResidentWorkgroups;
-  int n = num_splits > 0 ? num_splits : choose_splits(units, max_tiles, resident);
+  int n = num_splits > 0 ? num_splits : choose_splits(units, max_tiles);
   return std::max(1, n);
 }
 

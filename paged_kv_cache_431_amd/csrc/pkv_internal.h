@@ -12,11 +12,8 @@ constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kTileTokens = 16;        // tokens per matrix-core tile
 constexpr int kMaxGroup = 16;          // query heads per KV head handled by one workgroup
 // Waves per SIMD the matrix-core decode kernel is built for (its register
-// budget: 512 / this many VGPRs per lane), and the workgroups of it an
-// MI355X holds at once (256 compute units x 4 SIMDs x waves per SIMD / waves
-// per workgroup).  Only used to size the split over blocks.
+// budget: 512 / this many VGPRs per lane).
 constexpr int kDecodeWavesPerSimd = 3;
-constexpr int kResidentDecodeWorkgroups = 256 * 4 * kDecodeWavesPerSimd / kDecodeWaves;
 
 struct DecodeLaunch {
   void* out;
