@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("345108dad911761128dfcf161b4c637c953ca6001ef339ca34636a43b56e0035", "gqa70b-bf16-47x825-step", 1): 163103245,
-    ("345108dad911761128dfcf161b4c637c953ca6001ef339ca34636a43b56e0035", "gqa70b-bf16-47x825", 1): 162721792,
-    ("345108dad911761128dfcf161b4c637c953ca6001ef339ca34636a43b56e0035", "gqa70b-bf16-47x825-multi4", 1): 171791035,
+    ("d0d9542b67471f4f50ff86f5b8fb2c864b8f12b4f54b0ff4d845bae04a1ae39b", "gqa70b-bf16-47x825-step", 1): 163116504,
+    ("d0d9542b67471f4f50ff86f5b8fb2c864b8f12b4f54b0ff4d845bae04a1ae39b", "gqa70b-bf16-47x825", 1): 162704384,
+    ("d0d9542b67471f4f50ff86f5b8fb2c864b8f12b4f54b0ff4d845bae04a1ae39b", "gqa70b-bf16-47x825-multi4", 1): 169735019,
 }
 
 
