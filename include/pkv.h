@@ -147,9 +147,9 @@ int pkv_paged_attention_decode(void* out, int out_dtype,
  *                 (x / k_scale or x / v_scale).  A sequence with context
  *                 length 0 has no new token and gets output 0.
  *   other arguments as for pkv_paged_attention_decode (same workspace).
- * Supported: the matrix-core combinations of decode; others return
- *   PKV_EUNSUPPORTED (use the two calls).  Errors as for decode, plus
- *   PKV_EINVAL for NULL new_k / new_v with S > 0.
+ * Supported: the matrix-core combinations of decode, with new_k / new_v
+ *   under 2 GiB each; others return PKV_EUNSUPPORTED (use the two calls).
+ *   Errors as for decode, plus PKV_EINVAL for NULL new_k / new_v with S > 0.
  * ------------------------------------------------------------------------ */
 int pkv_decode_step(void* out, int out_dtype, const void* q, int q_dtype, const void* new_k, const void* new_v,
                     int new_dtype, void* k_cache, void* v_cache, int kv_dtype, float k_scale, float v_scale,

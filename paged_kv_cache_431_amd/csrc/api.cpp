@@ -144,6 +144,10 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
     if (!valid_dtype(new_dtype)) return PKV_EINVAL;
     const bool enc_ok = new_dtype == kv_dtype || (kv_dtype == PKV_FP8_E4M3 && new_dtype != PKV_FP8_E4M3);
     if (!enc_ok) return PKV_EUNSUPPORTED;
+    // the kernel addresses new_k / new_v through 32-bit buffer offsets
+    const int64_t new_bytes = (int64_t)num_seqs * h_kv * head_dim *
+                              (new_dtype == PKV_F32 ? 4 : (new_dtype == PKV_FP8_E4M3 ? 1 : 2));
+    if (new_bytes > INT32_MAX) return PKV_EUNSUPPORTED;
   }
 
   const int n = multi ? resolve_multi_splits(num_seqs, h_q, h_kv, max_query_len, max_context_len, num_splits)

@@ -497,30 +497,10 @@ decode_mfma_kernel(Params p) {
     MergeSmem<D> merge;
   } sm;
 
-  // Decode step: the new token's K and V rows of this (sequence, KV head) do
-  // not depend on the context length, so every wave loads them first and
-  // they arrive with it (the wave that turns out to own the last position
-  // uses them).  Lane l < 2 CH holds 8 elements (K chunks, then V chunks); every
-  // lane loads (the others repeat the last chunk), so the compiler counts
-  // this load with the ones after it.
-  constexpr int CH = D / 8;
-  c8_u32x4 nraw0 = {0u, 0u, 0u, 0u}, nraw1 = {0u, 0u, 0u, 0u};
-  if constexpr (AP) {
-    const int l = min((int)(threadIdx.x & 63), 2 * CH - 1);
-    const bool is_v = l >= CH;
-    const int unit = min(decode_unit(p), p.units - 1);
-    const size_t elem = (size_t)unit * D + (is_v ? l - CH : l) * 8;  // rows are [S, h_kv] in unit order
-    const uint8_t* src = is_v ? p.new_v : p.new_k;
-    if (p.new_dtype == kF32) {
-      nraw0 = *reinterpret_cast<const c8_u32x4*>(src + elem * 4);
-      nraw1 = *reinterpret_cast<const c8_u32x4*>(src + elem * 4 + 16);
-    } else if (p.new_dtype == kFP8) {
-      const c8_u32x2 x = *reinterpret_cast<const c8_u32x2*>(src + elem);
-      nraw0 = c8_u32x4{x[0], x[1], 0u, 0u};
-    } else {
-      nraw0 = *reinterpret_cast<const c8_u32x4*>(src + elem * 2);
-    }
-  }
+  constexpr int CH = D / 8;  // 8-element chunks of a row
+  // decode step: the new token's rows as loaded, 8 bytes at a time, from
+  // new_k (kx) and new_v (vx); a lane's chunk is the OR of the two
+  u32x2 kx[4] = {}, vx[4] = {};
 
   Item it;
   if (!get_item<MT, RT>(p, it)) return;
@@ -575,6 +555,8 @@ decode_mfma_kernel(Params p) {
   // the new token's rows converted to the pool's element type, into the
   // owner wave's LDS copy (K row, then V row)
   auto stage_new_token = [&]() {
+    const c8_u32x4 nraw0 = {kx[0][0] | vx[0][0], kx[0][1] | vx[0][1], kx[1][0] | vx[1][0], kx[1][1] | vx[1][1]};
+    const c8_u32x4 nraw1 = {kx[2][0] | vx[2][0], kx[2][1] | vx[2][1], kx[3][0] | vx[3][0], kx[3][1] | vx[3][1]};
     if (lane < 2 * CH) {
       const bool is_v = lane >= CH;
       uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][(is_v ? lane - CH : lane) * 8 * Tile::ES];
@@ -818,10 +800,37 @@ decode_mfma_kernel(Params p) {
     // Lane j holds the physical block of tile t0 + j (clamped into the chunk,
     // so only table entries of blocks the context covers are read).
     const int ids = bt_row[(t0 + min(lane, cn - 1)) >> p.tile_shift];
-    // decode step: the owner stages the new token here, where the wave waits
-    // for the block ids anyway (that load is the youngest)
+    // Decode step: every wave loads its (sequence, KV head)'s new K and V rows
+    // right after the chunk's block ids, so waiting for the ids (L2-resident)
+    // never waits for these (cold) rows, and before the chunk's first tile,
+    // whose loads they arrive with; the wave that owns the last position uses
+    // them (a wave with several chunks loads them again, 512 bytes a chunk).
+    // Lane l < CH holds 8 elements of K, lane CH + l those of V (the rest
+    // none).  The loads are unconditional, whatever the element type (a
+    // branch here would make the compiler drain every load in flight, and so
+    // would loads placed before the loop): each lane reads 32
+    // bytes at its chunk, 8 at a time, through buffer resources over new_k and
+    // new_v, whose range check returns zeros past the arrays' end and for the
+    // lanes a resource does not serve (chunks and arrays are multiples of 8
+    // bytes, so no 8-byte read straddles the end); 8 elements take the first
+    // 8, 16 or 32 bytes.
     if constexpr (AP) {
-      if (c0 == 0 && owner) stage_new_token();
+      // wave-uniform (kept in scalar registers: a resource built from vector
+      // registers would need a loop over the distinct values)
+      const int es = __builtin_amdgcn_readfirstlane(p.new_dtype == kF32 ? 4 : (p.new_dtype == kFP8 ? 1 : 2));
+      const int bytes = __builtin_amdgcn_readfirstlane(p.units * D * es);  // [S, h_kv, D]
+      const int row = __builtin_amdgcn_readfirstlane((it.s * p.h_kv + it.kvh) * D * es);
+      const int off_k = lane < CH ? row + lane * 8 * es : bytes;
+      const int off_v = lane >= CH && lane < 2 * CH ? row + (lane - CH) * 8 * es : bytes;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_k), (short)0, bytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_v), (short)0, bytes, kBufferWord3);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        kx[w] = kv_load8<false>(rk, off_k, 8 * w);
+        vx[w] = kv_load8<false>(rv, off_v, 8 * w);
+      }
     }
 
     // jr: the ring step's tile of the chunk (wave-uniform); jr >= cn past the
@@ -888,6 +897,8 @@ decode_mfma_kernel(Params p) {
     }
     if constexpr (AP) {
       if (owner && c0 + cn == n_my) last_phys = __builtin_amdgcn_readlane(ids, cn - 1);
+      // the owner stages the new token once its first tile is in flight
+      if (c0 == 0 && owner) stage_new_token();
     }
     for (int i = 0; i < cn; i += NBUF) {
 #pragma unroll

@@ -194,4 +194,5 @@ def test_decode_step_rejects_bad_arguments_without_launching():
     assert call(nd=2, kv=0, wsb=1 << 30) == pkv.PKV_EUNSUPPORTED  # fp32 pool: vector path, no fused step
     assert call(bs=8, wsb=1 << 30) == pkv.PKV_EINVAL         # 64 tokens do not fit 4 blocks of 8
     assert call(wsb=16) == pkv.PKV_EWORKSPACE
+    assert call(S=1 << 22, wsb=1 << 40) == pkv.PKV_EUNSUPPORTED   # new rows past 2 GiB (32-bit offsets)
     assert call(S=0, nk=None) == pkv.PKV_OK
