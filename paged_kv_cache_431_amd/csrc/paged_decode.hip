@@ -715,10 +715,21 @@ decode_mfma_kernel(Params p) {
       float s[4];
       // causal limit of this lane's row within the tile (several query tokens)
       const int row_cut = MT ? min(lim, row_lim[k] - r.tok0) : lim;
+      if constexpr (MT) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        s[rr] = sc[k][rr] * p.scale_log2;
-        if ((MT || partial) && 4 * q4 + rr >= row_cut) s[rr] = kNegInf;
+        for (int rr = 0; rr < 4; ++rr) {
+          s[rr] = sc[k][rr] * p.scale_log2;
+          if (4 * q4 + rr >= row_cut) s[rr] = kNegInf;
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) s[rr] = sc[k][rr] * p.scale_log2;
+        if (partial) {       // wave-uniform: full decode tiles skip the selects
+          asm volatile("");  // keeps this a branch instead of selects on every tile
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (4 * q4 + rr >= row_cut) s[rr] = kNegInf;
+        }
       }
       // Each lane tests its own 4 scores against its row's running max.  Only
       // when a lane of the wave exceeds it by more than the slack (always for
