@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("d0d9542b67471f4f50ff86f5b8fb2c864b8f12b4f54b0ff4d845bae04a1ae39b", "gqa70b-bf16-47x825-step", 1): 163116504,
-    ("d0d9542b67471f4f50ff86f5b8fb2c864b8f12b4f54b0ff4d845bae04a1ae39b", "gqa70b-bf16-47x825", 1): 162704384,
-    ("d0d9542b67471f4f50ff86f5b8fb2c864b8f12b4f54b0ff4d845bae04a1ae39b", "gqa70b-bf16-47x825-multi4", 1): 169735019,
+    ("6e5484751f70542e1f7f20ed560cc2eb157ff8d69948bdf42c5c3694537df87c", "gqa70b-bf16-47x825-step", 1): 163096060,
+    ("6e5484751f70542e1f7f20ed560cc2eb157ff8d69948bdf42c5c3694537df87c", "gqa70b-bf16-47x825", 1): 162706432,
+    ("6e5484751f70542e1f7f20ed560cc2eb157ff8d69948bdf42c5c3694537df87c", "gqa70b-bf16-47x825-multi4", 1): 169734917,
 }
 
 
