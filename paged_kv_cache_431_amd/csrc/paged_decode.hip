@@ -9,15 +9,16 @@
 // a KV head and reads each K/V byte once.
 //
 // Work decomposition
-//   One workgroup (4 waves) per (sequence, KV head, split).  The sequence's
+//   One workgroup (4 waves) per (sequence, KV head, split), and with several
+//   query tokens per (sequence, KV head, row group, split).  The sequence's
 //   16-token tiles are cut into `n` contiguous ranges (n <= num_splits, chosen
 //   per sequence on the device from its own length); each wave takes a
 //   contiguous quarter of its workgroup's range.  Each wave keeps an
 //   online-softmax state (running max m, running sum l, unnormalised output
 //   acc) per query row; the 4 waves merge through LDS; a sequence with several
 //   ranges writes partial states to the workspace and the last workgroup to
-//   finish (an atomic counter per (sequence, KV head)) merges them and writes
-//   the output, so a call is a single kernel launch.
+//   finish (an atomic counter per (sequence, KV head, row tile)) merges them
+//   and writes the output, so a call is a single kernel launch.
 //
 // Memory pipeline (the kernel is bound by HBM bandwidth: each K/V byte is
 // used by G query rows only)
@@ -29,8 +30,10 @@
 //   16-bit caches each tile's loads go through a buffer resource sized to the
 //   tile, and a ring step past the wave's last tile gets a resource of size
 //   0, whose loads return zeros without a memory access; with FP8 caches such
-//   a step re-reads the last tile.  Either way it computes nothing.  Decode's
-//   K/V loads are non-temporal: nothing re-reads them.
+//   a step re-reads the last tile.  Either way it computes nothing.  When one
+//   workgroup is the only reader of a (sequence, KV head)'s K/V (decode, and
+//   several query tokens held by one row group) the loads are non-temporal:
+//   nothing re-reads them.
 //
 // Matrix-core path (16-bit or FP8 caches, block_size 16 x 2^k)
 //   Scores: S^T[token][g] = K[token][:] . Q[g][:] with v_mfma_f32_16x16x32
@@ -54,9 +57,10 @@
 //   FP8 (OCP E4M3) K/V are converted in registers by the hardware converter
 //   (exact into bf16/f16); k_scale folds into the logit scale and v_scale
 //   into the final normalisation.
-//   Tokens past the context (the tail of the last block) are masked by select,
-//   never by multiplying, so whatever those slots hold (NaN included) cannot
-//   leak into the result.
+//   Tokens past the context (the tail of the last block) are masked by select
+//   (V rows zeroed, scores set to -inf), never by multiplying, so whatever
+//   those slots hold (NaN included) cannot leak into the result; tiles with
+//   no such token branch around the selects.
 //   The running max moves only when a score exceeds it by more than
 //   kRescaleSlack (log2 units), so after the first tiles the accumulators are
 //   rarely rescaled; probabilities relative to the stale max stay <= 2^8.
@@ -70,8 +74,9 @@
 // Several new query tokens per sequence (MT)
 //   The 16 MFMA columns hold (query token, query head) rows of a 16-row tile
 //   instead of the group's heads; each lane masks scores past its row's
-//   causal limit, and the row tiles of one (sequence, KV head) run on one XCD
-//   so that their walks of its K/V share that XCD's L2.
+//   causal limit.  A workgroup holds up to two row tiles (RT), so one walk
+//   of the K/V serves 32 rows; when a (sequence, KV head) has more row groups
+//   than one, they run on one XCD so that their walks share that XCD's L2.
 //
 // Decode step (AP): the new tokens' scatter inside the launch
 //   The one wave that reads a sequence's last position writes the new token
@@ -135,13 +140,14 @@ struct Item {
 // Workgroup id -> work item.  Consecutive workgroup ids go to the 8 XCDs in
 // turn, so every split of one (sequence, KV head) gets an id with the same
 // residue mod 8: their partial results meet in one XCD's L2.  With several
-// query tokens (MT) the row tiles of one (sequence, KV head) share that
+// query tokens (MT) the row groups of one (sequence, KV head) share that
 // residue too, so they read its K/V through the same L2.
 //
 // Query token i of the m new tokens of a sequence with ctx cached tokens
 // (its own K/V included) sits at position ctx - m + i and attends to the
 // positions up to and including its own.
-// Workgroup id -> unit index (decode: the (sequence, KV head) index).
+// Workgroup id -> unit index (decode: the (sequence, KV head) index; with
+// several query tokens the (sequence, KV head, row group) index).
 __device__ __forceinline__ int decode_unit(const Params& p) {
   const int wg = blockIdx.x;
   return ((wg >> 3) / p.num_splits) * 8 + (wg & 7);
