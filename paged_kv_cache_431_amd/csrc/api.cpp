@@ -50,6 +50,21 @@ int choose_splits(int64_t units, int64_t max_tiles) {
   return best;
 }
 
+// Balanced ranges for decode (the grid, or 0 for one workgroup per
+// (sequence, KV head, split)): when few pairs (at most two per CU) carry long
+// contexts (256 tiles or more), one workgroup per pair and split leaves the
+// work as uneven as the context lengths; equal ranges of all pairs' tiles do
+// not (32K-token FP8 batch: the longest wave had twice the median's tiles).
+// Only when the split count is the library's choice, for at most
+// kBalancedMaxSeqs sequences, and with all tiles countable in an int.
+int balanced_workgroups(int num_seqs, int h_kv, int max_context_len, int num_splits) {
+  const int64_t units = (int64_t)num_seqs * h_kv;
+  const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
+  if (num_splits > 0 || num_seqs > pkv::kBalancedMaxSeqs || units > kResidentWorkgroups || max_tiles < 256) return 0;
+  if (units * max_tiles >= INT32_MAX) return 0;
+  return (int)std::min<int64_t>(kResidentWorkgroups, ceil_div(units * max_tiles, pkv::kBalancedMinRange));
+}
+
 int resolve_splits(int num_seqs, int h_kv, int max_context_len, int num_splits) {
   const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
   int n = num_splits > 0 ? num_splits : choose_splits((int64_t)num_seqs * h_kv, max_tiles);
@@ -155,8 +170,9 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   const int row_tiles = multi ? pkv::multi_row_tiles(h_q, h_kv, max_query_len) : 1;
   const int row_groups = multi ? pkv::multi_row_groups(row_tiles) : 1;
   if ((int64_t)ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_groups * n > INT32_MAX) return PKV_EUNSUPPORTED;
+  const int balanced = !multi && matrix_core ? balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits) : 0;
   const pkv::WorkspaceLayout L = multi ? pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n)
-                                       : pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n);
+                                       : pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n, balanced);
   if (workspace_bytes < L.total) return PKV_EWORKSPACE;
 
   const double s = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)head_dim);
@@ -194,6 +210,8 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   a.new_dtype = new_dtype;
   a.k_scale_enc = k_scale;
   a.v_scale_enc = v_scale;
+  a.balanced_workgroups = balanced;
+  a.max_context_len = max_context_len;
   const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
@@ -219,14 +237,20 @@ int pkv_abi_version(void) { return PKV_ABI_VERSION; }
 int pkv_decode_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_context_len,
                           int num_splits) {
   if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return 0;
+  const int balanced = balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits);
+  if (balanced > 0) return (int)ceil_div(balanced, (int64_t)num_seqs * h_kv);  // workgroups per pair, on average
   return resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
 }
 
 size_t pkv_decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
                                   int max_context_len, int num_splits) {
   if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return 0;
+  // enough for either assignment (the balanced one is used on the
+  // matrix-core path only, which the shape alone does not tell)
   const int n = resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
-  return pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n).total;
+  const int balanced = balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits);
+  return std::max(pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n).total,
+                  pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n, balanced).total);
 }
 
 int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,

@@ -119,6 +119,8 @@ struct Params {
   // sequence s are [query_start[s], query_start[s + 1]) of q and out.
   const int32_t* query_start;
   int num_query_tokens, max_query_len;
+  int balanced;    // decode: tiles of all (sequence, KV head) pairs cut into gridDim.x equal ranges
+  int max_ctx;     // balanced ranges: context lengths are taken at most this
   int row_tiles;   // 16-row tiles of (query token, head) rows per (sequence, KV head)
   int row_groups;  // workgroups per (sequence, KV head, split): row_tiles / RT, rounded up
   // Decode step that appends each sequence's new token itself (null
@@ -135,6 +137,9 @@ struct Params {
 struct Item {
   int s, kvh, unit, split, ctx, n_tiles, n_splits_seq, t_begin, t_end;
   int rt, m, q0;  // several query tokens: first row tile, query tokens of the sequence, first query row
+  // balanced ranges (bal_r > 0): range length, first workgroup holding a
+  // piece of this pair, first tile of the pair in the flattened order
+  int bal_r, bal_w0, bal_p;
 };
 
 // Workgroup id -> work item.  Consecutive workgroup ids go to the 8 XCDs in
@@ -192,6 +197,7 @@ __device__ __forceinline__ bool get_item(const Params& p, Item& it) {
   const int per = it.n_splits_seq > 0 ? (it.n_tiles + it.n_splits_seq - 1) / it.n_splits_seq : 0;
   it.t_begin = it.split * per;
   it.t_end = min(it.n_tiles, it.t_begin + per);
+  it.bal_r = 0;
   return true;
 }
 
@@ -320,8 +326,20 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
     return;
   }
   const size_t base = (size_t)cidx * p.num_splits * R + g;  // partial row of split 0
+  // partial row of piece sp: split sp of the pair, or with balanced ranges
+  // slot 0 (first item) or 1 (last item) of workgroup bal_w0 + sp: the pair
+  // is the first item of every workgroup after bal_w0, and of bal_w0 only if
+  // it starts where that workgroup's range starts
+  auto prow_of = [&](int sp) -> size_t {
+    if (it.bal_r > 0) {
+      const int w = it.bal_w0 + sp;
+      const int slot = (sp > 0 || it.bal_p == w * it.bal_r) ? 0 : 1;
+      return ((size_t)w * 2 + slot) * R + g;
+    }
+    return base + (size_t)sp * R;
+  };
   if (row_ok) {
-    const size_t prow = base + (size_t)it.split * R;
+    const size_t prow = prow_of(it.split);
     float* dst = p.ws_acc + prow * D + chunk * DW;
 #pragma unroll
     for (int e = 0; e < DW; ++e) store_agent(dst + e, a[e]);
@@ -342,13 +360,13 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
   if (!sm.flag) return;
   if (!row_ok) return;
   float mm = kNegInf;
-  for (int sp = 0; sp < it.n_splits_seq; ++sp) mm = fmaxf(mm, load_agent(p.ws_ml + 2 * (base + (size_t)sp * R)));
+  for (int sp = 0; sp < it.n_splits_seq; ++sp) mm = fmaxf(mm, load_agent(p.ws_ml + 2 * prow_of(sp)));
   float ll = 0.f;
   float o[DW];
 #pragma unroll
   for (int e = 0; e < DW; ++e) o[e] = 0.f;
   for (int sp = 0; sp < it.n_splits_seq; ++sp) {
-    const size_t prow = base + (size_t)sp * R;
+    const size_t prow = prow_of(sp);
     const float m_i = load_agent(p.ws_ml + 2 * prow);
     const float l_i = load_agent(p.ws_ml + 2 * prow + 1);
     const float f = mm == kNegInf ? 0.f : fast_exp2(m_i - mm);
@@ -358,6 +376,117 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
     for (int e = 0; e < DW; ++e) o[e] += f * load_agent(src + e);
   }
   store_out<D>(p, row, chunk, o, ll > 0.f ? p.v_scale / ll : 0.f);
+}
+
+// Balanced ranges (decode with long contexts over few (sequence, KV head)
+// pairs, where one workgroup per pair and split leaves the work uneven): the
+// tiles of all pairs, pair after pair in (sequence, KV head) order, are cut
+// into equal contiguous ranges, one per workgroup, so every workgroup reads
+// the same number of bytes whatever the mix of context lengths.  A range may
+// hold the end of one pair, whole pairs and the start of another: each is an
+// item of its own, run one after the other; the pieces of a pair split over
+// several workgroups meet through the workspace as splits do.
+struct Balanced {
+  int S, H, cap;  // sequences, KV heads, context lengths taken at most this
+  int r;          // tiles per range (0: this workgroup has none)
+  int pos, end;   // this workgroup's next flattened tile and its range end
+};
+
+// pre (LDS, S + 1 entries) receives the prefix sums of the sequences' tile
+// counts; every thread of the workgroup calls this.
+__device__ void balanced_setup(const Params& p, int* pre, Balanced& b) {
+  b.S = p.units / p.h_kv;
+  b.H = p.h_kv;
+  // the host bounds all pairs' tiles at max_context_len each within int
+  b.cap = min(p.max_blocks_per_seq * p.block_size, p.max_ctx);
+  const int S = b.S, cap = b.cap;
+  auto seq_tiles = [&](int s) {
+    int c = p.context_lens[s];
+    c = c < 0 ? 0 : (c > cap ? cap : c);
+    return (c + kTileTokens - 1) / kTileTokens;
+  };
+  if (threadIdx.x < 64) {  // wave 0: pre[s] = tiles of sequences 0 .. s-1
+    const int lane = threadIdx.x;
+    const int per = (S + 63) / 64;  // consecutive sequences per lane
+    int sum = 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = lane * per + i;
+      if (s < S) sum += seq_tiles(s);
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    int run = incl - sum;
+    for (int i = 0; i < per; ++i) {
+      const int s = lane * per + i;
+      if (s < S) {
+        run += seq_tiles(s);
+        pre[s + 1] = run;
+      }
+    }
+    if (lane == 0) pre[0] = 0;
+  }
+  __syncthreads();
+  const int T = b.H * pre[S];  // every pair's tiles
+  // ranges of at least kBalancedMinRange tiles: with short contexts the
+  // later workgroups get nothing
+  const int w_eff = T > 0 ? min((int)gridDim.x, (T + kBalancedMinRange - 1) / kBalancedMinRange) : 0;
+  b.r = w_eff > 0 ? (T + w_eff - 1) / w_eff : 0;
+  const int w = blockIdx.x;
+  b.pos = w < w_eff ? w * b.r : 0;
+  b.end = w < w_eff ? min(T, b.pos + b.r) : 0;
+}
+
+// The next item of this workgroup's range, false when the range is done.
+__device__ bool balanced_next(const Params& p, const int* pre, Balanced& b, Item& it) {
+  if (b.pos >= b.end) return false;
+  const int H = b.H;
+  // the sequence whose pairs hold flattened tile pos: the last s with
+  // H pre[s] <= pos (sequences without tiles hold none)
+  int lo = 0, hi = b.S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (H * pre[mid] <= b.pos) lo = mid;
+    else hi = mid - 1;
+  }
+  const int ts = pre[lo + 1] - pre[lo];  // > 0: pos lies in it
+  const int kvh = (b.pos - H * pre[lo]) / ts;
+  const int first = H * pre[lo] + kvh * ts;  // the pair's first flattened tile
+  it.s = lo;
+  it.kvh = kvh;
+  it.unit = lo * H + kvh;
+  const int ctx = p.context_lens[lo];
+  it.ctx = ctx < 0 ? 0 : (ctx > b.cap ? b.cap : ctx);
+  it.n_tiles = ts;
+  it.t_begin = b.pos - first;
+  it.t_end = min(ts, b.end - first);
+  it.bal_r = b.r;
+  it.bal_w0 = first / b.r;
+  it.bal_p = first;
+  it.n_splits_seq = (first + ts - 1) / b.r - it.bal_w0 + 1;
+  it.split = blockIdx.x - it.bal_w0;
+  it.rt = 0;
+  it.m = 1;
+  it.q0 = 0;
+  b.pos = first + it.t_end;
+  return true;
+}
+
+// Pairs of sequences without tiles (context 0) get zeros.
+template <int D>
+__device__ void balanced_zeros(const Params& p, const int* pre, const Balanced& b) {
+  for (int u = blockIdx.x; u < p.units; u += gridDim.x) {
+    const int s = u / b.H;
+    if (pre[s + 1] == pre[s]) {
+      Item z;
+      z.s = s;
+      z.kvh = u - s * b.H;
+      write_zeros<D, false>(p, z, 0);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- matrix-core path
@@ -476,9 +605,10 @@ struct MfmaTile {
 // with two, one walk of the K/V serves 32 rows, at 2 waves per SIMD for the
 // registers of both tiles' states.  STREAM: K/V loads are non-temporal (the
 // only walk of each (sequence, KV head)); false when several workgroups walk
-// the same K/V and share it through L2.
-template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM>
-__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(RT == 1 ? kDecodeWavesPerSimd : 2))) void
+// the same K/V and share it through L2.  BAL: balanced ranges (decode only;
+// at most two workgroups per CU, so 2 waves per SIMD and their registers).
+template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM, bool BAL>
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(RT == 1 && !BAL ? kDecodeWavesPerSimd : 2))) void
 decode_mfma_kernel(Params p) {
   using Tile = MfmaTile<KV, D>;
   constexpr int ROW = Tile::ROW;
@@ -503,462 +633,481 @@ decode_mfma_kernel(Params p) {
     MergeSmem<D> merge;
   } sm;
 
+  // balanced ranges: prefix sums of the sequences' tile counts
+  __shared__ int sm_pre[BAL ? kBalancedMaxSeqs + 1 : 1];
+
   constexpr int CH = D / 8;  // 8-element chunks of a row
   // decode step: the new token's rows as loaded, 8 bytes at a time, from
   // new_k (kx) and new_v (vx); a lane's chunk is the OR of the two
   u32x2 kx[4] = {}, vx[4] = {};
 
-  Item it;
-  if (!get_item<MT, RT>(p, it)) return;
-  if (it.n_tiles == 0) {
-    if (it.split == 0) {
+  // One work item: a (sequence, KV head[, row group]) and a range of its
+  // tiles; every early return below leaves the item, not the kernel.
+  auto run_item = [&](Item& it) {
+    if (it.n_tiles == 0) {
+      if (it.split == 0) {
 #pragma unroll
-      for (int k = 0; k < RT; ++k) write_zeros<D, MT>(p, it, k);
-    }
-    return;
-  }
-  if (it.split >= it.n_splits_seq) return;
-
-  const int lane = threadIdx.x & 63;
-  // wave-uniform (the compiler cannot tell on its own), so every per-wave
-  // quantity below lives in scalar registers and the tile loop is uniform
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lo16 = lane & 15;
-  const int q4 = lane >> 4;
-  const int G = p.group;
-
-  // Q as the B operand: column lo16 of row tile k is row lo16 of that tile (a
-  // query head; with several query tokens a (query token, head) pair), same
-  // d order as the K chunks.  Padding rows hold zeros and never form an
-  // address outside the item's rows.  row_lim: positions [0, row_lim) the
-  // row attends to.
-  u32x4 qop[RT][NK];
-  int row_lim[RT];
-#pragma unroll
-  for (int k = 0; k < RT; ++k) {
-    bool row_ok;
-    size_t qr;
-    row_lim[k] = it.ctx;
-    if constexpr (MT) {
-      const int gr = (it.rt + k) * 16 + lo16;
-      const int i = gr / G;
-      row_ok = i < it.m;
-      const int ic = row_ok ? i : it.m - 1;  // it.m >= 1 for an item with rows
-      qr = (size_t)(it.q0 + ic) * p.h_q + it.kvh * G + (row_ok ? gr - i * G : 0);
-      row_lim[k] = min(it.ctx, max(0, it.ctx - it.m + ic + 1));
-    } else {
-      row_ok = lo16 < G;
-      qr = (size_t)it.s * p.h_q + it.kvh * G + (row_ok ? lo16 : G - 1);
-    }
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const int d0 = KV == kFP8 ? 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1) : 32 * kk + 8 * q4;
-      qop[k][kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // the new token's rows converted to the pool's element type, into the
-  // owner wave's LDS copy (K row, then V row)
-  auto stage_new_token = [&]() {
-    const c8_u32x4 nraw0 = {kx[0][0] | vx[0][0], kx[0][1] | vx[0][1], kx[1][0] | vx[1][0], kx[1][1] | vx[1][1]};
-    const c8_u32x4 nraw1 = {kx[2][0] | vx[2][0], kx[2][1] | vx[2][1], kx[3][0] | vx[3][0], kx[3][1] | vx[3][1]};
-    if (lane < 2 * CH) {
-      const bool is_v = lane >= CH;
-      uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][(is_v ? lane - CH : lane) * 8 * Tile::ES];
-      if constexpr (KV == kFP8) {
-        const float enc = is_v ? p.v_scale_enc : p.k_scale_enc;
-        Chunk8<kFP8> x;
-        if (p.new_dtype == kF32) {
-          Chunk8<kF32> c;
-          c.w[0] = nraw0;
-          c.w[1] = nraw1;
-          x = quantize8<kF32>(c, enc);
-        } else if (p.new_dtype == kF16) {
-          Chunk8<kF16> c;
-          c.w = nraw0;
-          x = quantize8<kF16>(c, enc);
-        } else if (p.new_dtype == kBF16) {
-          Chunk8<kBF16> c;
-          c.w = nraw0;
-          x = quantize8<kBF16>(c, enc);
-        } else {
-          x.w = c8_u32x2{nraw0[0], nraw0[1]};
-        }
-        store8<kFP8>(stage, x);
-      } else {
-        Chunk8<KV> x;
-        x.w = nraw0;
-        store8<KV>(stage, x);
+        for (int k = 0; k < RT; ++k) write_zeros<D, MT>(p, it, k);
       }
+      return;
     }
-  };
+    if (it.split >= it.n_splits_seq) return;
 
-  f32x4 acc[RT][NT];
-  float m_run[RT], l_run[RT];
-#pragma unroll
-  for (int k = 0; k < RT; ++k) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[k][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[k] = kNegInf;
-    l_run[k] = 0.f;
-  }
+    const int lane = threadIdx.x & 63;
+    // wave-uniform (the compiler cannot tell on its own), so every per-wave
+    // quantity below lives in scalar registers and the tile loop is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lo16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int G = p.group;
 
-  // This wave's tiles: a contiguous slice [wb, wb + n_my) of the range.
-  const int span = it.t_end - it.t_begin;
-  const int per_w = span > 0 ? (span + kDecodeWaves - 1) / kDecodeWaves : 0;
-  const int wb = it.t_begin + wave * per_w;
-  const int n_my = max(0, min(it.t_end, wb + per_w) - wb);
-
-  const int32_t* bt_row = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
-  const size_t head_bytes = (size_t)p.block_size * ROW;
-  const size_t block_bytes = head_bytes * p.h_kv;
-  const uint8_t* k_head = p.k_cache + it.kvh * head_bytes;
-  const uint8_t* v_head = p.v_cache + it.kvh * head_bytes;
-  const int k_lane = lane * 16;                           // K: 16 bytes of each 1 KiB piece
-  const int v_lane = (4 * q4) * ROW + lo16 * Tile::VB;    // V: row 4 q4 + rr, chunk lo16
-
-  // Decode step: the wave whose tiles include the sequence's last position
-  // (the last tile of the last split) appends the new token: it computes
-  // that tile with the new rows (staged in LDS at the start) in place of the
-  // loaded ones, and writes them to the pool after its last tile.  No other
-  // wave or workgroup reads that position, so nothing waits for the write.
-  const bool owner = AP && it.t_end == it.n_tiles && wb <= it.n_tiles - 1 && it.n_tiles - 1 < wb + n_my;
-  const int last_tok0 = (it.n_tiles - 1) * kTileTokens;
-  int last_phys = -1;  // physical block of the last position (owner wave)
-
-  auto compute_tile = [&](Tile& r, bool valid) {
-    const int lim = valid ? r.lim : 0;
-    // 0) K rows into the wave's LDS tile (lane l of load c holds chunk
-    //    l % LPR of row RPK c + l / LPR)
-    uint8_t* kt = reinterpret_cast<uint8_t*>(sm.t.ktile[wave]);
-#pragma unroll
-    for (int c = 0; c < KCH; ++c)
-      *reinterpret_cast<u32x4*>(kt + (Tile::RPK * c + lane / Tile::LPR) * Tile::KLDS + (lane % Tile::LPR) * 16) =
-          r.k[c];
-    if constexpr (AP) {
-      if (owner && valid && r.tok0 == last_tok0) {  // the tile holding the new token (wave-uniform)
-        const int row = it.ctx - 1 - r.tok0;
-        if (lane < Tile::LPR) {
-          *reinterpret_cast<u32x4*>(kt + row * Tile::KLDS + lane * 16) =
-              *reinterpret_cast<const u32x4*>(&sm.t.newrow[wave][0][lane * 16]);
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if (4 * q4 + rr == row) {
-#pragma unroll
-            for (int w = 0; w < VDW; ++w)
-              r.v[rr][w] = *reinterpret_cast<const uint32_t*>(&sm.t.newrow[wave][1][lo16 * Tile::VB + 4 * w]);
-          }
-        }
-      }
-    }
-    // K in the operand layout: lane (lo16, q4) holds chunk q4 + 4 c of row lo16
-    u32x4 kr[KCH];
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) kr[c] = *reinterpret_cast<const u32x4*>(kt + lo16 * Tile::KLDS + (q4 + 4 * c) * 16);
-    // 1) scores for the 16 tokens of the tile against each (padded) row tile
-    f32x4 sc[RT];
-#pragma unroll
-    for (int k = 0; k < RT; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      u32x4 a;
-      if constexpr (KV == kFP8) {
-        const uint32_t w0 = kr[kk >> 1][2 * (kk & 1)], w1 = kr[kk >> 1][2 * (kk & 1) + 1];
-        a = u32x4{fp8x2_to_pair<CT, false>(w0), fp8x2_to_pair<CT, true>(w0), fp8x2_to_pair<CT, false>(w1),
-                  fp8x2_to_pair<CT, true>(w1)};
-      } else {
-        a = kr[kk];
-      }
-#pragma unroll
-      for (int k = 0; k < RT; ++k) sc[k] = mfma_16x16x32<CT>(a, qop[k][kk], sc[k]);
-    }
-    mfma_guard();
-
-    // 2) V -> LDS in its natural layout; masked rows are zeroed first
-    const bool partial = lim < kTileTokens;
-    if (partial) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (4 * q4 + rr >= lim) {
-#pragma unroll
-          for (int w = 0; w < VDW; ++w) r.v[rr][w] = 0u;
-        }
-    }
-    // Row t of the tile, 16-byte chunk c sits at chunk c ^ swz(t) of row t:
-    // the transposed reads below then touch all banks evenly.
-    auto vt_chunk = [&](int t, int c) { return t * VCH + (c ^ ((t & (VCH / 2 - 1)) << 1)); };
-    u32x4* vt = sm.t.vtile[wave];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int t = 4 * q4 + rr;  // this lane holds d = lo16 * D/16 ... of row t
-      uint32_t w16[D / 32];       // those D/16 elements as 16-bit pairs
-      if constexpr (KV == kFP8) {
-#pragma unroll
-        for (int w = 0; w < VDW; ++w) {
-          w16[2 * w] = fp8x2_to_pair<CT, false>(r.v[rr][w]);
-          w16[2 * w + 1] = fp8x2_to_pair<CT, true>(r.v[rr][w]);
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < VDW; ++w) w16[w] = r.v[rr][w];
-      }
-      if constexpr (D == 128) {
-        vt[vt_chunk(t, lo16)] = u32x4{w16[0], w16[1], w16[2], w16[3]};
-      } else {
-        reinterpret_cast<u32x2*>(vt + vt_chunk(t, lo16 >> 1))[lo16 & 1] = u32x2{w16[0], w16[1]};
-      }
-    }
-    compiler_fence();
-
-    // 3) online softmax (log2 domain), per row tile; row g = lo16, tokens
-    //    4*q4 + rr; probabilities of those tokens as hi + lo 16-bit parts
-    //    (p = hi + lo + O(2^-16 p)), the B operands of the PV products
-    u32x2 p_hi[RT], p_lo[RT];
+    // Q as the B operand: column lo16 of row tile k is row lo16 of that tile (a
+    // query head; with several query tokens a (query token, head) pair), same
+    // d order as the K chunks.  Padding rows hold zeros and never form an
+    // address outside the item's rows.  row_lim: positions [0, row_lim) the
+    // row attends to.
+    u32x4 qop[RT][NK];
+    int row_lim[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      float s[4];
-      // causal limit of this lane's row within the tile (several query tokens)
-      const int row_cut = MT ? min(lim, row_lim[k] - r.tok0) : lim;
+      bool row_ok;
+      size_t qr;
+      row_lim[k] = it.ctx;
       if constexpr (MT) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          s[rr] = sc[k][rr] * p.scale_log2;
-          if (4 * q4 + rr >= row_cut) s[rr] = kNegInf;
-        }
+        const int gr = (it.rt + k) * 16 + lo16;
+        const int i = gr / G;
+        row_ok = i < it.m;
+        const int ic = row_ok ? i : it.m - 1;  // it.m >= 1 for an item with rows
+        qr = (size_t)(it.q0 + ic) * p.h_q + it.kvh * G + (row_ok ? gr - i * G : 0);
+        row_lim[k] = min(it.ctx, max(0, it.ctx - it.m + ic + 1));
       } else {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) s[rr] = sc[k][rr] * p.scale_log2;
-        if (partial) {       // wave-uniform: full decode tiles skip the selects
-          asm volatile("");  // keeps this a branch instead of selects on every tile
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            if (4 * q4 + rr >= row_cut) s[rr] = kNegInf;
-        }
+        row_ok = lo16 < G;
+        qr = (size_t)it.s * p.h_q + it.kvh * G + (row_ok ? lo16 : G - 1);
       }
-      // Each lane tests its own 4 scores against its row's running max.  Only
-      // when a lane of the wave exceeds it by more than the slack (always for
-      // the first tile with a finite score) are the row maxima formed across
-      // the 4 lanes of each row and the state rescaled; otherwise the tile
-      // needs no cross-lane step at all.
-      const float mx_lane = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      if (__builtin_amdgcn_ballot_w64(mx_lane > m_run[k] + kRescaleSlack) != 0) {
-        float mx = fmaxf(mx_lane, shfl_xor_f32(mx_lane, 16));
-        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-        const bool grow = mx > m_run[k] + kRescaleSlack;  // the same on the 4 lanes of a row
-        const float m_new = grow ? mx : m_run[k];
-        const float alpha = grow ? fast_exp2(m_run[k] - m_new) : 1.f;  // 0 when m_run is -inf
-        l_run[k] *= alpha;
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[k][n] *= alpha;
-        m_run[k] = m_new;
-      }
-      const float m_use = m_run[k] == kNegInf ? 0.f : m_run[k];
-      float pr[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) pr[rr] = fast_exp2(s[rr] - m_use);
-      l_run[k] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-
-      if constexpr (CT == kBF16) {
-        float lo_part[4];
-        uint32_t hb[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          hb[rr] = __float_as_uint(pr[rr]) & 0xffff0000u;
-          lo_part[rr] = pr[rr] - __uint_as_float(hb[rr]);
-        }
-        p_hi[k] = u32x2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
-                        __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
-        p_lo[k] = u32x2{__builtin_amdgcn_perm(__float_as_uint(lo_part[1]), __float_as_uint(lo_part[0]), 0x07060302u),
-                        __builtin_amdgcn_perm(__float_as_uint(lo_part[3]), __float_as_uint(lo_part[2]), 0x07060302u)};
-      } else {
-        const auto h01 = __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]);
-        const auto h23 = __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]);
-        const auto l01 = __builtin_amdgcn_cvt_pkrtz(pr[0] - (float)h01[0], pr[1] - (float)h01[1]);
-        const auto l23 = __builtin_amdgcn_cvt_pkrtz(pr[2] - (float)h23[0], pr[3] - (float)h23[1]);
-        p_hi[k] = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
-        p_lo[k] = u32x2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+      for (int kk = 0; kk < NK; ++kk) {
+        const int d0 = KV == kFP8 ? 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1) : 32 * kk + 8 * q4;
+        qop[k][kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 
-    // 4) O^T += V^T P^T: per 16 rows of d, two 16x16x16 MFMAs (hi and lo
-    //    parts of P) whose A operand is the 8-byte V^T cell of 4 tokens
-    // A operands by transposing reads: lane (4k + m) of each 16-lane group
-    // points at 4 elements d = 16n + 4m .. +3 of token 4*q4 + k, and lane j
-    // receives element j of those 4 tokens' rows, i.e. V^T[16n + j][4*q4 .. +3]
-    u32x2 cell[NT];
-    {
-      const int t = 4 * q4 + (lo16 >> 2);
-      const int m = lo16 & 3;
-      typedef __attribute__((address_space(3))) char lds_char;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        lds_char* a = (lds_char*)(vt + vt_chunk(t, 2 * n + (m >> 1))) + 8 * (m & 1);
-        cell[n] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                (__attribute__((address_space(3))) v4i16*)a));
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < RT; ++k) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[k][n] = mfma_16x16x16<CT>(cell[n], p_hi[k], acc[k][n]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[k][n] = mfma_16x16x16<CT>(cell[n], p_lo[k], acc[k][n]);
-    }
-    mfma_guard();
-    compiler_fence();
-  };
-
-  for (int c0 = 0; c0 < n_my; c0 += 64) {
-    const int cn = min(64, n_my - c0);  // tiles in this chunk (>= 1)
-    const int t0 = wb + c0;             // its first tile
-    // Lane j holds the physical block of tile t0 + j (clamped into the chunk,
-    // so only table entries of blocks the context covers are read).
-    const int ids = bt_row[(t0 + min(lane, cn - 1)) >> p.tile_shift];
-    // Decode step: every wave loads its (sequence, KV head)'s new K and V rows
-    // right after the chunk's block ids, so waiting for the ids (L2-resident)
-    // never waits for these (cold) rows, and before the chunk's first tile,
-    // whose loads they arrive with; the wave that owns the last position uses
-    // them (a wave with several chunks loads them again, 512 bytes a chunk).
-    // Lane l < CH holds 8 elements of K, lane CH + l those of V (the rest
-    // none).  The loads are unconditional, whatever the element type (a
-    // branch here would make the compiler drain every load in flight, and so
-    // would loads placed before the loop): each lane reads 32
-    // bytes at its chunk, 8 at a time, through buffer resources over new_k and
-    // new_v, whose range check returns zeros past the arrays' end and for the
-    // lanes a resource does not serve (chunks and arrays are multiples of 8
-    // bytes, so no 8-byte read straddles the end); 8 elements take the first
-    // 8, 16 or 32 bytes.
-    if constexpr (AP) {
-      // wave-uniform (kept in scalar registers: a resource built from vector
-      // registers would need a loop over the distinct values)
-      const int es = __builtin_amdgcn_readfirstlane(p.new_dtype == kF32 ? 4 : (p.new_dtype == kFP8 ? 1 : 2));
-      const int bytes = __builtin_amdgcn_readfirstlane(p.units * D * es);  // [S, h_kv, D]
-      const int row = __builtin_amdgcn_readfirstlane((it.s * p.h_kv + it.kvh) * D * es);
-      const int off_k = lane < CH ? row + lane * 8 * es : bytes;
-      const int off_v = lane >= CH && lane < 2 * CH ? row + (lane - CH) * 8 * es : bytes;
-      const __amdgpu_buffer_rsrc_t rk =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_k), (short)0, bytes, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t rv =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_v), (short)0, bytes, kBufferWord3);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        kx[w] = kv_load8<false>(rk, off_k, 8 * w);
-        vx[w] = kv_load8<false>(rv, off_v, 8 * w);
-      }
-    }
-
-    // jr: the ring step's tile of the chunk (wave-uniform); jr >= cn past the
-    // end, where the loads return zeros without a memory access
-    auto load_tile = [&](Tile& r, int jr) {
-      const int j = min(jr, cn - 1);
-      const int tok0 = (t0 + j) * kTileTokens;
-      int phys = __builtin_amdgcn_readlane(ids, j);
-      const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
-      phys = ok ? phys : 0;
-      const int rem = it.ctx - tok0;
-      r.lim = ok ? (rem < kTileTokens ? rem : kTileTokens) : 0;
-      r.tok0 = tok0;
-      const int sub = (t0 + j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
-      const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
-      if constexpr (KV != kFP8) {
-        const int bytes = ok && jr < cn ? kTileTokens * ROW : 0;
-        const __amdgpu_buffer_rsrc_t kr =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k_head + off), (short)0, bytes, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t vr =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(v_head + off), (short)0, bytes, kBufferWord3);
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) r.k[c] = kv_load16<STREAM>(kr, k_lane, c * 1024);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if constexpr (VDW == 4) {
-            const u32x4 x = kv_load16<STREAM>(vr, v_lane, rr * ROW);
-            r.v[rr][0] = x[0];
-            r.v[rr][1] = x[1];
-            r.v[rr][2] = x[2];
-            r.v[rr][3] = x[3];
+    // the new token's rows converted to the pool's element type, into the
+    // owner wave's LDS copy (K row, then V row)
+    auto stage_new_token = [&]() {
+      const c8_u32x4 nraw0 = {kx[0][0] | vx[0][0], kx[0][1] | vx[0][1], kx[1][0] | vx[1][0], kx[1][1] | vx[1][1]};
+      const c8_u32x4 nraw1 = {kx[2][0] | vx[2][0], kx[2][1] | vx[2][1], kx[3][0] | vx[3][0], kx[3][1] | vx[3][1]};
+      if (lane < 2 * CH) {
+        const bool is_v = lane >= CH;
+        uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][(is_v ? lane - CH : lane) * 8 * Tile::ES];
+        if constexpr (KV == kFP8) {
+          const float enc = is_v ? p.v_scale_enc : p.k_scale_enc;
+          Chunk8<kFP8> x;
+          if (p.new_dtype == kF32) {
+            Chunk8<kF32> c;
+            c.w[0] = nraw0;
+            c.w[1] = nraw1;
+            x = quantize8<kF32>(c, enc);
+          } else if (p.new_dtype == kF16) {
+            Chunk8<kF16> c;
+            c.w = nraw0;
+            x = quantize8<kF16>(c, enc);
+          } else if (p.new_dtype == kBF16) {
+            Chunk8<kBF16> c;
+            c.w = nraw0;
+            x = quantize8<kBF16>(c, enc);
           } else {
-            const u32x2 x = kv_load8<STREAM>(vr, v_lane, rr * ROW);
-            r.v[rr][0] = x[0];
-            r.v[rr][1] = x[1];
+            x.w = c8_u32x2{nraw0[0], nraw0[1]};
           }
-        }
-      } else {
-        const uint8_t* kp = k_head + off + k_lane;
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) r.k[c] = kv_gload<STREAM, u32x4>(kp + c * 1024);
-        const uint8_t* vp = v_head + off + v_lane;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if constexpr (VDW == 2) {
-            const u32x2 x = kv_gload<STREAM, u32x2>(vp + rr * ROW);
-            r.v[rr][0] = x[0];
-            r.v[rr][1] = x[1];
-          } else {
-            r.v[rr][0] = kv_gload<STREAM, uint32_t>(vp + rr * ROW);
-          }
+          store8<kFP8>(stage, x);
+        } else {
+          Chunk8<KV> x;
+          x.w = nraw0;
+          store8<KV>(stage, x);
         }
       }
     };
 
-    // Ring of NBUF buffers: tile i + NBUF - 1 is loaded while tile i is computed.
-    Tile buf[NBUF];
+    f32x4 acc[RT][NT];
+    float m_run[RT], l_run[RT];
 #pragma unroll
-    for (int b = 0; b < NBUF - 1; ++b) {
-      load_tile(buf[b], b);
-      // keep the tiles' loads in ring order, so that waiting for the oldest
-      // tile never waits for a younger one
+    for (int k = 0; k < RT; ++k) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[k][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run[k] = kNegInf;
+      l_run[k] = 0.f;
+    }
+
+    // This wave's tiles: a contiguous slice [wb, wb + n_my) of the range.
+    const int span = it.t_end - it.t_begin;
+    const int per_w = span > 0 ? (span + kDecodeWaves - 1) / kDecodeWaves : 0;
+    const int wb = it.t_begin + wave * per_w;
+    const int n_my = max(0, min(it.t_end, wb + per_w) - wb);
+
+    const int32_t* bt_row = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
+    const size_t head_bytes = (size_t)p.block_size * ROW;
+    const size_t block_bytes = head_bytes * p.h_kv;
+    const uint8_t* k_head = p.k_cache + it.kvh * head_bytes;
+    const uint8_t* v_head = p.v_cache + it.kvh * head_bytes;
+    const int k_lane = lane * 16;                           // K: 16 bytes of each 1 KiB piece
+    const int v_lane = (4 * q4) * ROW + lo16 * Tile::VB;    // V: row 4 q4 + rr, chunk lo16
+
+    // Decode step: the wave whose tiles include the sequence's last position
+    // (the last tile of the last split) appends the new token: it computes
+    // that tile with the new rows (staged in LDS at the start) in place of the
+    // loaded ones, and writes them to the pool after its last tile.  No other
+    // wave or workgroup reads that position, so nothing waits for the write.
+    const bool owner = AP && it.t_end == it.n_tiles && wb <= it.n_tiles - 1 && it.n_tiles - 1 < wb + n_my;
+    const int last_tok0 = (it.n_tiles - 1) * kTileTokens;
+    int last_phys = -1;  // physical block of the last position (owner wave)
+
+    auto compute_tile = [&](Tile& r, bool valid) {
+      const int lim = valid ? r.lim : 0;
+      // 0) K rows into the wave's LDS tile (lane l of load c holds chunk
+      //    l % LPR of row RPK c + l / LPR)
+      uint8_t* kt = reinterpret_cast<uint8_t*>(sm.t.ktile[wave]);
+#pragma unroll
+      for (int c = 0; c < KCH; ++c)
+        *reinterpret_cast<u32x4*>(kt + (Tile::RPK * c + lane / Tile::LPR) * Tile::KLDS + (lane % Tile::LPR) * 16) =
+            r.k[c];
+      if constexpr (AP) {
+        if (owner && valid && r.tok0 == last_tok0) {  // the tile holding the new token (wave-uniform)
+          const int row = it.ctx - 1 - r.tok0;
+          if (lane < Tile::LPR) {
+            *reinterpret_cast<u32x4*>(kt + row * Tile::KLDS + lane * 16) =
+                *reinterpret_cast<const u32x4*>(&sm.t.newrow[wave][0][lane * 16]);
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            if (4 * q4 + rr == row) {
+#pragma unroll
+              for (int w = 0; w < VDW; ++w)
+                r.v[rr][w] = *reinterpret_cast<const uint32_t*>(&sm.t.newrow[wave][1][lo16 * Tile::VB + 4 * w]);
+            }
+          }
+        }
+      }
+      // K in the operand layout: lane (lo16, q4) holds chunk q4 + 4 c of row lo16
+      u32x4 kr[KCH];
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) kr[c] = *reinterpret_cast<const u32x4*>(kt + lo16 * Tile::KLDS + (q4 + 4 * c) * 16);
+      // 1) scores for the 16 tokens of the tile against each (padded) row tile
+      f32x4 sc[RT];
+#pragma unroll
+      for (int k = 0; k < RT; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        u32x4 a;
+        if constexpr (KV == kFP8) {
+          const uint32_t w0 = kr[kk >> 1][2 * (kk & 1)], w1 = kr[kk >> 1][2 * (kk & 1) + 1];
+          a = u32x4{fp8x2_to_pair<CT, false>(w0), fp8x2_to_pair<CT, true>(w0), fp8x2_to_pair<CT, false>(w1),
+                    fp8x2_to_pair<CT, true>(w1)};
+        } else {
+          a = kr[kk];
+        }
+#pragma unroll
+        for (int k = 0; k < RT; ++k) sc[k] = mfma_16x16x32<CT>(a, qop[k][kk], sc[k]);
+      }
+      mfma_guard();
+
+      // 2) V -> LDS in its natural layout; masked rows are zeroed first
+      const bool partial = lim < kTileTokens;
+      if (partial) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (4 * q4 + rr >= lim) {
+#pragma unroll
+            for (int w = 0; w < VDW; ++w) r.v[rr][w] = 0u;
+          }
+      }
+      // Row t of the tile, 16-byte chunk c sits at chunk c ^ swz(t) of row t:
+      // the transposed reads below then touch all banks evenly.
+      auto vt_chunk = [&](int t, int c) { return t * VCH + (c ^ ((t & (VCH / 2 - 1)) << 1)); };
+      u32x4* vt = sm.t.vtile[wave];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = 4 * q4 + rr;  // this lane holds d = lo16 * D/16 ... of row t
+        uint32_t w16[D / 32];       // those D/16 elements as 16-bit pairs
+        if constexpr (KV == kFP8) {
+#pragma unroll
+          for (int w = 0; w < VDW; ++w) {
+            w16[2 * w] = fp8x2_to_pair<CT, false>(r.v[rr][w]);
+            w16[2 * w + 1] = fp8x2_to_pair<CT, true>(r.v[rr][w]);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < VDW; ++w) w16[w] = r.v[rr][w];
+        }
+        if constexpr (D == 128) {
+          vt[vt_chunk(t, lo16)] = u32x4{w16[0], w16[1], w16[2], w16[3]};
+        } else {
+          reinterpret_cast<u32x2*>(vt + vt_chunk(t, lo16 >> 1))[lo16 & 1] = u32x2{w16[0], w16[1]};
+        }
+      }
+      compiler_fence();
+
+      // 3) online softmax (log2 domain), per row tile; row g = lo16, tokens
+      //    4*q4 + rr; probabilities of those tokens as hi + lo 16-bit parts
+      //    (p = hi + lo + O(2^-16 p)), the B operands of the PV products
+      u32x2 p_hi[RT], p_lo[RT];
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        float s[4];
+        // causal limit of this lane's row within the tile (several query tokens)
+        const int row_cut = MT ? min(lim, row_lim[k] - r.tok0) : lim;
+        if constexpr (MT) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            s[rr] = sc[k][rr] * p.scale_log2;
+            if (4 * q4 + rr >= row_cut) s[rr] = kNegInf;
+          }
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) s[rr] = sc[k][rr] * p.scale_log2;
+          if (partial) {       // wave-uniform: full decode tiles skip the selects
+            asm volatile("");  // keeps this a branch instead of selects on every tile
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (4 * q4 + rr >= row_cut) s[rr] = kNegInf;
+          }
+        }
+        // Each lane tests its own 4 scores against its row's running max.  Only
+        // when a lane of the wave exceeds it by more than the slack (always for
+        // the first tile with a finite score) are the row maxima formed across
+        // the 4 lanes of each row and the state rescaled; otherwise the tile
+        // needs no cross-lane step at all.
+        const float mx_lane = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        if (__builtin_amdgcn_ballot_w64(mx_lane > m_run[k] + kRescaleSlack) != 0) {
+          float mx = fmaxf(mx_lane, shfl_xor_f32(mx_lane, 16));
+          mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+          const bool grow = mx > m_run[k] + kRescaleSlack;  // the same on the 4 lanes of a row
+          const float m_new = grow ? mx : m_run[k];
+          const float alpha = grow ? fast_exp2(m_run[k] - m_new) : 1.f;  // 0 when m_run is -inf
+          l_run[k] *= alpha;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[k][n] *= alpha;
+          m_run[k] = m_new;
+        }
+        const float m_use = m_run[k] == kNegInf ? 0.f : m_run[k];
+        float pr[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) pr[rr] = fast_exp2(s[rr] - m_use);
+        l_run[k] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+        if constexpr (CT == kBF16) {
+          float lo_part[4];
+          uint32_t hb[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            hb[rr] = __float_as_uint(pr[rr]) & 0xffff0000u;
+            lo_part[rr] = pr[rr] - __uint_as_float(hb[rr]);
+          }
+          p_hi[k] = u32x2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                          __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
+          p_lo[k] = u32x2{__builtin_amdgcn_perm(__float_as_uint(lo_part[1]), __float_as_uint(lo_part[0]), 0x07060302u),
+                          __builtin_amdgcn_perm(__float_as_uint(lo_part[3]), __float_as_uint(lo_part[2]), 0x07060302u)};
+        } else {
+          const auto h01 = __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]);
+          const auto h23 = __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]);
+          const auto l01 = __builtin_amdgcn_cvt_pkrtz(pr[0] - (float)h01[0], pr[1] - (float)h01[1]);
+          const auto l23 = __builtin_amdgcn_cvt_pkrtz(pr[2] - (float)h23[0], pr[3] - (float)h23[1]);
+          p_hi[k] = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+          p_lo[k] = u32x2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+        }
+      }
+
+      // 4) O^T += V^T P^T: per 16 rows of d, two 16x16x16 MFMAs (hi and lo
+      //    parts of P) whose A operand is the 8-byte V^T cell of 4 tokens
+      // A operands by transposing reads: lane (4k + m) of each 16-lane group
+      // points at 4 elements d = 16n + 4m .. +3 of token 4*q4 + k, and lane j
+      // receives element j of those 4 tokens' rows, i.e. V^T[16n + j][4*q4 .. +3]
+      u32x2 cell[NT];
+      {
+        const int t = 4 * q4 + (lo16 >> 2);
+        const int m = lo16 & 3;
+        typedef __attribute__((address_space(3))) char lds_char;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          lds_char* a = (lds_char*)(vt + vt_chunk(t, 2 * n + (m >> 1))) + 8 * (m & 1);
+          cell[n] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                  (__attribute__((address_space(3))) v4i16*)a));
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[k][n] = mfma_16x16x16<CT>(cell[n], p_hi[k], acc[k][n]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[k][n] = mfma_16x16x16<CT>(cell[n], p_lo[k], acc[k][n]);
+      }
+      mfma_guard();
+      compiler_fence();
+    };
+
+    for (int c0 = 0; c0 < n_my; c0 += 64) {
+      const int cn = min(64, n_my - c0);  // tiles in this chunk (>= 1)
+      const int t0 = wb + c0;             // its first tile
+      // Lane j holds the physical block of tile t0 + j (clamped into the chunk,
+      // so only table entries of blocks the context covers are read).
+      const int ids = bt_row[(t0 + min(lane, cn - 1)) >> p.tile_shift];
+      // Decode step: every wave loads its (sequence, KV head)'s new K and V rows
+      // right after the chunk's block ids, so waiting for the ids (L2-resident)
+      // never waits for these (cold) rows, and before the chunk's first tile,
+      // whose loads they arrive with; the wave that owns the last position uses
+      // them (a wave with several chunks loads them again, 512 bytes a chunk).
+      // Lane l < CH holds 8 elements of K, lane CH + l those of V (the rest
+      // none).  The loads are unconditional, whatever the element type (a
+      // branch here would make the compiler drain every load in flight, and so
+      // would loads placed before the loop): each lane reads 32
+      // bytes at its chunk, 8 at a time, through buffer resources over new_k and
+      // new_v, whose range check returns zeros past the arrays' end and for the
+      // lanes a resource does not serve (chunks and arrays are multiples of 8
+      // bytes, so no 8-byte read straddles the end); 8 elements take the first
+      // 8, 16 or 32 bytes.
+      if constexpr (AP) {
+        // wave-uniform (kept in scalar registers: a resource built from vector
+        // registers would need a loop over the distinct values)
+        const int es = __builtin_amdgcn_readfirstlane(p.new_dtype == kF32 ? 4 : (p.new_dtype == kFP8 ? 1 : 2));
+        const int bytes = __builtin_amdgcn_readfirstlane(p.units * D * es);  // [S, h_kv, D]
+        const int row = __builtin_amdgcn_readfirstlane((it.s * p.h_kv + it.kvh) * D * es);
+        const int off_k = lane < CH ? row + lane * 8 * es : bytes;
+        const int off_v = lane >= CH && lane < 2 * CH ? row + (lane - CH) * 8 * es : bytes;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_k), (short)0, bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_v), (short)0, bytes, kBufferWord3);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kx[w] = kv_load8<false>(rk, off_k, 8 * w);
+          vx[w] = kv_load8<false>(rv, off_v, 8 * w);
+        }
+      }
+
+      // jr: the ring step's tile of the chunk (wave-uniform); jr >= cn past the
+      // end, where the loads return zeros without a memory access
+      auto load_tile = [&](Tile& r, int jr) {
+        const int j = min(jr, cn - 1);
+        const int tok0 = (t0 + j) * kTileTokens;
+        int phys = __builtin_amdgcn_readlane(ids, j);
+        const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+        phys = ok ? phys : 0;
+        const int rem = it.ctx - tok0;
+        r.lim = ok ? (rem < kTileTokens ? rem : kTileTokens) : 0;
+        r.tok0 = tok0;
+        const int sub = (t0 + j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
+        const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
+        if constexpr (KV != kFP8) {
+          const int bytes = ok && jr < cn ? kTileTokens * ROW : 0;
+          const __amdgpu_buffer_rsrc_t kr =
+              __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k_head + off), (short)0, bytes, kBufferWord3);
+          const __amdgpu_buffer_rsrc_t vr =
+              __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(v_head + off), (short)0, bytes, kBufferWord3);
+#pragma unroll
+          for (int c = 0; c < KCH; ++c) r.k[c] = kv_load16<STREAM>(kr, k_lane, c * 1024);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            if constexpr (VDW == 4) {
+              const u32x4 x = kv_load16<STREAM>(vr, v_lane, rr * ROW);
+              r.v[rr][0] = x[0];
+              r.v[rr][1] = x[1];
+              r.v[rr][2] = x[2];
+              r.v[rr][3] = x[3];
+            } else {
+              const u32x2 x = kv_load8<STREAM>(vr, v_lane, rr * ROW);
+              r.v[rr][0] = x[0];
+              r.v[rr][1] = x[1];
+            }
+          }
+        } else {
+          const uint8_t* kp = k_head + off + k_lane;
+#pragma unroll
+          for (int c = 0; c < KCH; ++c) r.k[c] = kv_gload<STREAM, u32x4>(kp + c * 1024);
+          const uint8_t* vp = v_head + off + v_lane;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            if constexpr (VDW == 2) {
+              const u32x2 x = kv_gload<STREAM, u32x2>(vp + rr * ROW);
+              r.v[rr][0] = x[0];
+              r.v[rr][1] = x[1];
+            } else {
+              r.v[rr][0] = kv_gload<STREAM, uint32_t>(vp + rr * ROW);
+            }
+          }
+        }
+      };
+
+      // Ring of NBUF buffers: tile i + NBUF - 1 is loaded while tile i is computed.
+      Tile buf[NBUF];
+#pragma unroll
+      for (int b = 0; b < NBUF - 1; ++b) {
+        load_tile(buf[b], b);
+        // keep the tiles' loads in ring order, so that waiting for the oldest
+        // tile never waits for a younger one
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (AP) {
+        if (owner && c0 + cn == n_my) last_phys = __builtin_amdgcn_readlane(ids, cn - 1);
+        // the owner stages the new token once its first tile is in flight
+        if (c0 == 0 && owner) stage_new_token();
+      }
+      for (int i = 0; i < cn; i += NBUF) {
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+          load_tile(buf[(b + NBUF - 1) % NBUF], i + b + NBUF - 1);
+          compute_tile(buf[b], i + b < cn);
+        }
+      }
     }
+
     if constexpr (AP) {
-      if (owner && c0 + cn == n_my) last_phys = __builtin_amdgcn_readlane(ids, cn - 1);
-      // the owner stages the new token once its first tile is in flight
-      if (c0 == 0 && owner) stage_new_token();
-    }
-    for (int i = 0; i < cn; i += NBUF) {
-#pragma unroll
-      for (int b = 0; b < NBUF; ++b) {
-        load_tile(buf[(b + NBUF - 1) % NBUF], i + b + NBUF - 1);
-        compute_tile(buf[b], i + b < cn);
+      // the new token into its slot (its rows are still in LDS)
+      if (owner && (unsigned)last_phys < (unsigned)p.num_blocks && lane < 2 * CH) {
+        const bool is_v = lane >= CH;
+        const int c = is_v ? lane - CH : lane;
+        const int pos = it.ctx - 1;
+        const int off = pos - (pos / p.block_size) * p.block_size;
+        const size_t dst = (((size_t)last_phys * p.h_kv + it.kvh) * p.block_size + off) * ROW + c * 8 * Tile::ES;
+        const uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][c * 8 * Tile::ES];
+        uint8_t* cache = (is_v ? p.v_store : p.k_store) + dst;
+        if constexpr (KV == kFP8) {
+          store8<kFP8>(cache, load8<kFP8>(stage));
+        } else {
+          store8<KV>(cache, load8<KV>(stage));
+        }
       }
     }
-  }
 
-  if constexpr (AP) {
-    // the new token into its slot (its rows are still in LDS)
-    if (owner && (unsigned)last_phys < (unsigned)p.num_blocks && lane < 2 * CH) {
-      const bool is_v = lane >= CH;
-      const int c = is_v ? lane - CH : lane;
-      const int pos = it.ctx - 1;
-      const int off = pos - (pos / p.block_size) * p.block_size;
-      const size_t dst = (((size_t)last_phys * p.h_kv + it.kvh) * p.block_size + off) * ROW + c * 8 * Tile::ES;
-      const uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][c * 8 * Tile::ES];
-      uint8_t* cache = (is_v ? p.v_store : p.k_store) + dst;
-      if constexpr (KV == kFP8) {
-        store8<kFP8>(cache, load8<kFP8>(stage));
-      } else {
-        store8<KV>(cache, load8<KV>(stage));
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      float l_row = l_run[k] + shfl_xor_f32(l_run[k], 16);
+      l_row += shfl_xor_f32(l_row, 32);
+      // every wave is done with its tiles (first row tile) or the previous
+      // row tile's merge has read the LDS: reuse it
+      __syncthreads();
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(&sm.merge.acc[wave][lo16][16 * n + 4 * q4]) = acc[k][n];
+      if (q4 == 0) {
+        sm.merge.m[wave][lo16] = m_run[k];
+        sm.merge.l[wave][lo16] = l_row;
       }
+      __syncthreads();
+      finish<D, MT, RT>(p, it, k, sm.merge);
     }
-  }
+  };
 
-#pragma unroll
-  for (int k = 0; k < RT; ++k) {
-    float l_row = l_run[k] + shfl_xor_f32(l_run[k], 16);
-    l_row += shfl_xor_f32(l_row, 32);
-    // every wave is done with its tiles (first row tile) or the previous
-    // row tile's merge has read the LDS: reuse it
-    __syncthreads();
-#pragma unroll
-    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(&sm.merge.acc[wave][lo16][16 * n + 4 * q4]) = acc[k][n];
-    if (q4 == 0) {
-      sm.merge.m[wave][lo16] = m_run[k];
-      sm.merge.l[wave][lo16] = l_row;
+  Item it;
+  if constexpr (!BAL) {  // one item: a pair (row group) and split
+    if (!get_item<MT, RT>(p, it)) return;
+    run_item(it);
+  } else {  // the items of this workgroup's range, one after the other
+    Balanced bal;
+    balanced_setup(p, sm_pre, bal);
+    while (balanced_next(p, sm_pre, bal, it)) {
+      run_item(it);
+      __syncthreads();  // this item's merge is done with the LDS
     }
-    __syncthreads();
-    finish<D, MT, RT>(p, it, k, sm.merge);
+    balanced_zeros<D>(p, sm_pre, bal);
   }
 }
 
@@ -1063,16 +1212,16 @@ hipError_t launch(K kernel, int grid, const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool MT, bool AP, int RT, bool ST>
+template <int D, bool MT, bool AP, int RT, bool ST, bool BAL = false>
 hipError_t dispatch_mfma(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
   if (a.kv_dtype == kBF16 && a.q_dtype == kBF16)
-    return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP, RT, ST>, grid, p, s);
+    return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP, RT, ST, BAL>, grid, p, s);
   if (a.kv_dtype == kF16 && a.q_dtype == kF16)
-    return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP, RT, ST>, grid, p, s);
+    return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP, RT, ST, BAL>, grid, p, s);
   if (a.kv_dtype == kFP8 && a.q_dtype == kBF16)
-    return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP, RT, ST>, grid, p, s);
+    return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP, RT, ST, BAL>, grid, p, s);
   if (a.kv_dtype == kFP8 && a.q_dtype == kF16)
-    return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP, RT, ST>, grid, p, s);
+    return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP, RT, ST, BAL>, grid, p, s);
   return hipErrorInvalidValue;
 }
 
@@ -1091,10 +1240,12 @@ hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_
   }
   if (a.new_k != nullptr) {
     if (!a.matrix_core) return hipErrorInvalidValue;
-    return dispatch_mfma<D, false, true, 1, true>(a, grid, p, s);
+    return p.balanced ? dispatch_mfma<D, false, true, 1, true, true>(a, grid, p, s)
+                      : dispatch_mfma<D, false, true, 1, true>(a, grid, p, s);
   }
   if (a.matrix_core) {
-    return dispatch_mfma<D, false, false, 1, true>(a, grid, p, s);
+    return p.balanced ? dispatch_mfma<D, false, false, 1, true, true>(a, grid, p, s)
+                      : dispatch_mfma<D, false, false, 1, true>(a, grid, p, s);
   } else {
     if (a.kv_dtype == kF32 && a.q_dtype == kF32) return launch(decode_vector_kernel<kF32, kF32, D>, grid, p, s);
     if (a.kv_dtype == kBF16 && a.q_dtype == kBF16) return launch(decode_vector_kernel<kBF16, kBF16, D>, grid, p, s);
@@ -1107,10 +1258,13 @@ hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_
 
 }  // namespace
 
-WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits) {
+WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits,
+                                        int balanced_workgroups) {
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t units = (size_t)num_seqs * h_kv;
-  const size_t rows = (size_t)num_seqs * h_q * num_splits;  // units * G * splits
+  const size_t rows = balanced_workgroups > 0
+                          ? (size_t)balanced_workgroups * 2 * (h_q / h_kv)  // two slots per workgroup, G rows each
+                          : (size_t)num_seqs * h_q * num_splits;           // units * G * splits
   WorkspaceLayout L;
   L.counters = 0;
   L.ml = align(units * sizeof(int32_t));
@@ -1139,7 +1293,8 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const bool multi = a.query_start != nullptr;
   const int row_tiles = multi ? multi_row_tiles(a.h_q, a.h_kv, a.max_query_len) : 1;
   const WorkspaceLayout L = multi ? multi_workspace_layout(a.num_seqs, a.h_kv, a.head_dim, row_tiles, a.num_splits)
-                                  : decode_workspace_layout(a.num_seqs, a.h_q, a.h_kv, a.head_dim, a.num_splits);
+                                  : decode_workspace_layout(a.num_seqs, a.h_q, a.h_kv, a.head_dim, a.num_splits,
+                                                            a.balanced_workgroups);
   Params p;
   p.out = a.out;
   p.q = a.q;
@@ -1170,6 +1325,8 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.max_query_len = a.max_query_len;
   p.row_tiles = row_tiles;
   p.row_groups = multi ? multi_row_groups(row_tiles) : 1;
+  p.balanced = a.balanced_workgroups > 0 ? 1 : 0;
+  p.max_ctx = a.max_context_len;
   p.new_k = static_cast<const uint8_t*>(a.new_k);
   p.new_v = static_cast<const uint8_t*>(a.new_v);
   p.k_store = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
@@ -1177,7 +1334,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.new_dtype = a.new_dtype;
   p.k_scale_enc = a.k_scale_enc;
   p.v_scale_enc = a.v_scale_enc;
-  const int grid = ((p.units + 7) / 8) * 8 * p.row_groups * a.num_splits;
+  const int grid = p.balanced ? a.balanced_workgroups : ((p.units + 7) / 8) * 8 * p.row_groups * a.num_splits;
   if (grid == 0) return hipSuccess;
   if (a.head_dim == 128) return dispatch<128>(a, grid, p, stream);
   if (a.head_dim == 64) return dispatch<64>(a, grid, p, stream);

@@ -14,6 +14,11 @@ constexpr int kMaxGroup = 16;          // query heads per KV head handled by one
 // Waves per SIMD the matrix-core decode kernel is built for (its register
 // budget: 512 / this many VGPRs per lane).
 constexpr int kDecodeWavesPerSimd = 3;
+// Balanced ranges (decode over few (sequence, KV head) pairs with long
+// contexts): at most this many sequences (their tile counts' prefix sums sit
+// in LDS), and ranges of at least this many 16-token tiles.
+constexpr int kBalancedMaxSeqs = 1024;
+constexpr int kBalancedMinRange = 64;
 
 struct DecodeLaunch {
   void* out;
@@ -45,6 +50,11 @@ struct DecodeLaunch {
   const void* new_v;
   int new_dtype;
   float k_scale_enc, v_scale_enc;
+  // Balanced ranges (decode only, matrix-core path; 0 = one workgroup per
+  // (sequence, KV head, split)): the grid, every workgroup one equal range of
+  // all pairs' tiles; context lengths are taken at most max_context_len.
+  int balanced_workgroups;
+  int max_context_len;
 };
 
 // 16-row tiles of (query token, query head) rows per (sequence, KV head).
@@ -70,7 +80,10 @@ struct WorkspaceLayout {
   size_t total;
 };
 
-WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits);
+// balanced_workgroups > 0: the layout of balanced ranges (two partial-state
+// slots per workgroup) instead of one per (sequence, KV head, split).
+WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits,
+                                        int balanced_workgroups = 0);
 
 // Workspace of a call with several query tokens per sequence: one counter
 // and 16 partial-state rows per split for each (sequence, KV head, row tile),

@@ -48,6 +48,11 @@ def test_workspace_and_split_sizing():
     rows = 47 * 64 * n
     assert ws >= rows * 128 * 4 + rows * 8 + 47 * 8 * 4
     assert pkv.pkv_decode_workspace_bytes(47, 64, 8, 128, 16, 825, 5) >= 47 * 64 * 5 * 128 * 4
+    # 10 sequences of up to 12,000 tokens on 2 KV heads: balanced ranges over
+    # ceil(20 x 750 / 64) = 235 workgroups, two partial slots of 8 rows each
+    assert pkv.pkv_decode_workspace_bytes(10, 16, 2, 128, 16, 12000) >= 235 * 2 * 8 * (128 + 2) * 4
+    assert pkv.pkv_decode_num_splits(10, 16, 2, 128, 16, 12000) == 12       # 235 workgroups over 20 pairs
+    assert pkv.pkv_decode_num_splits(10, 16, 2, 128, 16, 12000, 3) == 3     # forced: one per pair and split
     assert pkv.pkv_decode_num_splits(47, 64, 8, 128, 16, 825, 5) == 5
     assert pkv.pkv_decode_num_splits(4, 8, 2, 64, 16, 0) == 1
     # invalid shapes size to 0
