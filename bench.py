@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("6e5484751f70542e1f7f20ed560cc2eb157ff8d69948bdf42c5c3694537df87c", "gqa70b-bf16-47x825-step", 1): 163096060,
-    ("6e5484751f70542e1f7f20ed560cc2eb157ff8d69948bdf42c5c3694537df87c", "gqa70b-bf16-47x825", 1): 162706432,
-    ("6e5484751f70542e1f7f20ed560cc2eb157ff8d69948bdf42c5c3694537df87c", "gqa70b-bf16-47x825-multi4", 1): 169734917,
+    ("85792e9014c4254c12ed13cc92c7b0db3f506884017e5d821ec94c65e04f07e7", "gqa70b-bf16-47x825-step", 1): 163099084,
+    ("85792e9014c4254c12ed13cc92c7b0db3f506884017e5d821ec94c65e04f07e7", "gqa70b-bf16-47x825", 1): 162720768,
+    ("85792e9014c4254c12ed13cc92c7b0db3f506884017e5d821ec94c65e04f07e7", "gqa70b-bf16-47x825-multi4", 1): 169744251,
 }
 
 
