@@ -65,6 +65,22 @@ int balanced_workgroups(int num_seqs, int h_kv, int max_context_len, int num_spl
   return (int)std::min<int64_t>(kResidentWorkgroups, ceil_div(units * max_tiles, pkv::kBalancedMinRange));
 }
 
+// Longest pairs first (the bin shift, or -1 for pairs in order): when a
+// decode grid of one workgroup per (sequence, KV head, split) does not fit on
+// the GPU at once, workgroups that start late should hold the short pairs.
+// Only when the split count is the library's choice, for at most
+// kLptMaxSeqs sequences (every workgroup ranks them all).
+int longest_first_shift(int num_seqs, int h_kv, int max_context_len, int num_splits, int chosen_splits,
+                        int row_groups, int waves_per_simd) {
+  const int64_t grid = ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_groups * chosen_splits;
+  if (num_splits > 0 || num_seqs > pkv::kLptMaxSeqs || grid <= (int64_t)pkv::kComputeUnits * waves_per_simd)
+    return -1;
+  const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
+  int shift = 0;
+  while ((max_tiles >> shift) >= pkv::kLptBins) ++shift;
+  return shift;
+}
+
 int resolve_splits(int num_seqs, int h_kv, int max_context_len, int num_splits) {
   const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
   int n = num_splits > 0 ? num_splits : choose_splits((int64_t)num_seqs * h_kv, max_tiles);
@@ -212,6 +228,12 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   a.v_scale_enc = v_scale;
   a.balanced_workgroups = balanced;
   a.max_context_len = max_context_len;
+  // resident workgroups per SIMD: 2 for the kernels holding two row tiles
+  const int waves_per_simd =
+      multi && pkv::multi_tiles_per_workgroup(row_tiles) == 2 ? 2 : pkv::kDecodeWavesPerSimd;
+  a.lpt_shift = matrix_core && balanced == 0 ? longest_first_shift(num_seqs, h_kv, max_context_len, num_splits, n,
+                                                                   row_groups, waves_per_simd)
+                                             : -1;
   const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

@@ -19,6 +19,9 @@
 //   ranges writes partial states to the workspace and the last workgroup to
 //   finish (an atomic counter per (sequence, KV head, row tile)) merges them
 //   and writes the output, so a call is a single kernel launch.
+//   When the grid does not fit on the GPU at once, workgroups take the
+//   sequences longest first (each workgroup ranks all context lengths in
+//   LDS), so the workgroups that start last hold the shortest work.
 //
 // Memory pipeline (the kernel is bound by HBM bandwidth: each K/V byte is
 // used by G query rows only)
@@ -119,6 +122,7 @@ struct Params {
   // sequence s are [query_start[s], query_start[s + 1]) of q and out.
   const int32_t* query_start;
   int num_query_tokens, max_query_len;
+  int lpt_shift;   // decode: >= 0 takes sequences longest first (tile counts >> lpt_shift), -1 in order
   int balanced;    // decode: tiles of all (sequence, KV head) pairs cut into gridDim.x equal ranges
   int max_ctx;     // balanced ranges: context lengths are taken at most this
   int row_tiles;   // 16-row tiles of (query token, head) rows per (sequence, KV head)
@@ -158,8 +162,98 @@ __device__ __forceinline__ int decode_unit(const Params& p) {
   return ((wg >> 3) / p.num_splits) * 8 + (wg & 7);
 }
 
-template <bool MT, int RT>
-__device__ __forceinline__ bool get_item(const Params& p, Item& it) {
+// Exclusive prefix sum of x over the workgroup's threads in thread order;
+// part holds kDecodeWaves ints.  Every thread calls this; part may be reused
+// after the next barrier.
+__device__ int block_exclusive_scan(int x, int* part) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) part[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int j = 0; j < w; ++j) base += part[j];
+  return base + incl - x;
+}
+
+// Longest pairs first.  Workgroups start in id order as resident ones
+// finish, so when the grid does not fit at once, handing the pairs out in
+// decreasing order of work lets the long ones start first and the short ones
+// fill the end (the longest-processing-time-first rule of list scheduling):
+// the launch no longer waits on a long pair that started late.  Rank r of
+// the sequences ordered by tile count (>> p.lpt_shift), longest first, ties
+// in index order; *ctx_out receives its context length, clamped as items
+// clamp it.  Every thread of the workgroup calls this (at most kLptMaxSeqs
+// sequences); lds holds kLptBins + 8 ints.
+__device__ int lpt_sequence(const Params& p, int r, int* lds, int* ctx_out) {
+  constexpr int PER = kLptMaxSeqs / kDecodeThreads;  // consecutive sequences per thread
+  constexpr int BPT = kLptBins / kDecodeThreads;     // bins per thread
+  int* hist = lds;              // sequences per bin
+  int* part = lds + kLptBins;   // [0, 4): scan partials; 4, 5: the rank's bin and its first rank; 6, 7: result
+  const int S = p.units / p.h_kv;
+  const int t = threadIdx.x;
+  const int cap = p.max_blocks_per_seq * p.block_size;
+  int bin[PER], ctx[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = t * PER + i;
+    int c = s < S ? p.context_lens[s] : 0;
+    c = c < 0 ? 0 : (c > cap ? cap : c);
+    ctx[i] = c;
+    bin[i] = s < S ? min(((c + kTileTokens - 1) / kTileTokens) >> p.lpt_shift, kLptBins - 1) : -1;
+  }
+  for (int b = t; b < kLptBins; b += kDecodeThreads) hist[b] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (bin[i] >= 0) atomicAdd(&hist[bin[i]], 1);
+  __syncthreads();
+  // thread t holds the bins [top - BPT, top), walked downwards: the
+  // sequences in higher bins than these come first
+  const int top = kLptBins - BPT * t;
+  int local = 0;
+#pragma unroll
+  for (int j = 1; j <= BPT; ++j) local += hist[top - j];
+  int run = block_exclusive_scan(local, part);
+#pragma unroll
+  for (int j = 1; j <= BPT; ++j) {
+    const int h = hist[top - j];
+    if (run <= r && r < run + h) {
+      part[4] = top - j;
+      part[5] = run;
+    }
+    run += h;
+  }
+  __syncthreads();
+  const int bstar = part[4];
+  const int k = r - part[5];  // rank r is the k-th sequence of bin bstar in index order
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) cnt += bin[i] == bstar;
+  int before = block_exclusive_scan(cnt, part);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (bin[i] == bstar) {
+      if (before == k) {
+        part[6] = t * PER + i;
+        part[7] = ctx[i];
+      }
+      ++before;
+    }
+  }
+  __syncthreads();
+  const int seq = part[6];
+  *ctx_out = part[7];
+  __syncthreads();  // the LDS is the walk's next
+  return seq;
+}
+
+template <bool MT, int RT, bool LPT = false>
+__device__ __forceinline__ bool get_item(const Params& p, Item& it, int* lds) {
   const int wg = blockIdx.x;
   const int j = wg >> 3;
   it.unit = decode_unit(p);
@@ -172,11 +266,22 @@ __device__ __forceinline__ bool get_item(const Params& p, Item& it) {
     base = (y / p.row_groups) * 8 + (it.unit & 7);
   }
   if (base >= p.units) return false;
-  it.s = base / p.h_kv;
-  it.kvh = base - it.s * p.h_kv;
-  int ctx = p.context_lens[it.s];
+  int ctx;
   const int cap = p.max_blocks_per_seq * p.block_size;
-  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+  if (LPT && p.lpt_shift >= 0) {  // (workgroup-uniform: every thread takes it)
+    // the unit's KV head (and row group) stay; its sequence is the one of
+    // that rank.  All splits and row groups of a unit take the same one.
+    const int kvh = base % p.h_kv;
+    it.s = lpt_sequence(p, base / p.h_kv, lds, &ctx);
+    base = it.s * p.h_kv + kvh;
+    if constexpr (MT) it.unit = ((base >> 3) * p.row_groups + it.rt / RT) * 8 + (base & 7);
+    else it.unit = base;
+  } else {
+    it.s = base / p.h_kv;
+    ctx = p.context_lens[it.s];
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+  }
+  it.kvh = base - it.s * p.h_kv;
   it.ctx = ctx;
   int n_tok = ctx;  // positions any row of the item attends to: [0, n_tok)
   if constexpr (MT) {
@@ -631,6 +736,7 @@ decode_mfma_kernel(Params p) {
       u32x4 ktile[kDecodeWaves][kTileTokens * Tile::KLDS / 16];
     } t;
     MergeSmem<D> merge;
+    int lpt[kLptBins + 8];  // longest pairs first: bins and scan partials (before the walk)
   } sm;
 
   // balanced ranges: prefix sums of the sequences' tile counts
@@ -1098,7 +1204,7 @@ decode_mfma_kernel(Params p) {
 
   Item it;
   if constexpr (!BAL) {  // one item: a pair (row group) and split
-    if (!get_item<MT, RT>(p, it)) return;
+    if (!get_item<MT, RT, true>(p, it, sm.lpt)) return;
     run_item(it);
   } else {  // the items of this workgroup's range, one after the other
     Balanced bal;
@@ -1132,7 +1238,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_vector_kernel(Params p)
   __shared__ MergeSmem<D> sm;
 
   Item it;
-  if (!get_item<false, 1>(p, it)) return;
+  if (!get_item<false, 1>(p, it, nullptr)) return;
   if (it.n_tiles == 0) {
     if (it.split == 0) write_zeros<D, false>(p, it, 0);
     return;
@@ -1326,6 +1432,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.row_tiles = row_tiles;
   p.row_groups = multi ? multi_row_groups(row_tiles) : 1;
   p.balanced = a.balanced_workgroups > 0 ? 1 : 0;
+  p.lpt_shift = a.lpt_shift;
   p.max_ctx = a.max_context_len;
   p.new_k = static_cast<const uint8_t*>(a.new_k);
   p.new_v = static_cast<const uint8_t*>(a.new_v);

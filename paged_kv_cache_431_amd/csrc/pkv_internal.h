@@ -19,6 +19,12 @@ constexpr int kDecodeWavesPerSimd = 3;
 // in LDS), and ranges of at least this many 16-token tiles.
 constexpr int kBalancedMaxSeqs = 1024;
 constexpr int kBalancedMinRange = 64;
+// Compute units of an MI355X.
+constexpr int kComputeUnits = 256;
+// Longest pairs first (decode grids that do not fit on the GPU at once): at
+// most this many sequences, ranked by tile count in this many bins (LDS).
+constexpr int kLptMaxSeqs = 1024;
+constexpr int kLptBins = 2048;
 
 struct DecodeLaunch {
   void* out;
@@ -55,6 +61,11 @@ struct DecodeLaunch {
   // all pairs' tiles; context lengths are taken at most max_context_len.
   int balanced_workgroups;
   int max_context_len;
+  // Longest pairs first (decode, one workgroup per (sequence, KV head,
+  // split)): -1 = workgroups take pairs in (sequence, KV head) order; else
+  // sequences are taken in decreasing order of their tile count shifted
+  // right by this many bits (ties in index order).
+  int lpt_shift = -1;
 };
 
 // 16-row tiles of (query token, query head) rows per (sequence, KV head).
