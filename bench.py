@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("85792e9014c4254c12ed13cc92c7b0db3f506884017e5d821ec94c65e04f07e7", "gqa70b-bf16-47x825-step", 1): 163099084,
-    ("85792e9014c4254c12ed13cc92c7b0db3f506884017e5d821ec94c65e04f07e7", "gqa70b-bf16-47x825", 1): 162720768,
-    ("85792e9014c4254c12ed13cc92c7b0db3f506884017e5d821ec94c65e04f07e7", "gqa70b-bf16-47x825-multi4", 1): 169744251,
+    ("db4bb28b08e47b9496e21f29381e4f2a44f4f0c034cd948399178c7471cad3a5", "gqa70b-bf16-47x825-step", 1): 163112346,
+    ("db4bb28b08e47b9496e21f29381e4f2a44f4f0c034cd948399178c7471cad3a5", "gqa70b-bf16-47x825", 1): 162693120,
+    ("db4bb28b08e47b9496e21f29381e4f2a44f4f0c034cd948399178c7471cad3a5", "gqa70b-bf16-47x825-multi4", 1): 169735270,
 }
 
 

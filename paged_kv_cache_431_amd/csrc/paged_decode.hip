@@ -268,7 +268,7 @@ __device__ __forceinline__ bool get_item(const Params& p, Item& it, int* lds) {
   if (base >= p.units) return false;
   int ctx;
   const int cap = p.max_blocks_per_seq * p.block_size;
-  if (LPT && p.lpt_shift >= 0) {  // (workgroup-uniform: every thread takes it)
+  if constexpr (LPT) {
     // the unit's KV head (and row group) stay; its sequence is the one of
     // that rank.  All splits and row groups of a unit take the same one.
     const int kvh = base % p.h_kv;
@@ -712,7 +712,7 @@ struct MfmaTile {
 // only walk of each (sequence, KV head)); false when several workgroups walk
 // the same K/V and share it through L2.  BAL: balanced ranges (decode only;
 // at most two workgroups per CU, so 2 waves per SIMD and their registers).
-template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM, bool BAL>
+template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM, bool BAL, bool LPT>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(RT == 1 && !BAL ? kDecodeWavesPerSimd : 2))) void
 decode_mfma_kernel(Params p) {
   using Tile = MfmaTile<KV, D>;
@@ -1204,7 +1204,7 @@ decode_mfma_kernel(Params p) {
 
   Item it;
   if constexpr (!BAL) {  // one item: a pair (row group) and split
-    if (!get_item<MT, RT, true>(p, it, sm.lpt)) return;
+    if (!get_item<MT, RT, LPT>(p, it, sm.lpt)) return;
     run_item(it);
   } else {  // the items of this workgroup's range, one after the other
     Balanced bal;
@@ -1318,17 +1318,28 @@ hipError_t launch(K kernel, int grid, const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool MT, bool AP, int RT, bool ST, bool BAL, bool LPT>
+hipError_t dispatch_mfma_types(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
+  if (a.kv_dtype == kBF16 && a.q_dtype == kBF16)
+    return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP, RT, ST, BAL, LPT>, grid, p, s);
+  if (a.kv_dtype == kF16 && a.q_dtype == kF16)
+    return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP, RT, ST, BAL, LPT>, grid, p, s);
+  if (a.kv_dtype == kFP8 && a.q_dtype == kBF16)
+    return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP, RT, ST, BAL, LPT>, grid, p, s);
+  if (a.kv_dtype == kFP8 && a.q_dtype == kF16)
+    return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP, RT, ST, BAL, LPT>, grid, p, s);
+  return hipErrorInvalidValue;
+}
+
+// Kernels with balanced ranges have no order to choose; the others are built
+// with and without the longest-first ranking, so that a launch that does not
+// rank runs no trace of it.
 template <int D, bool MT, bool AP, int RT, bool ST, bool BAL = false>
 hipError_t dispatch_mfma(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
-  if (a.kv_dtype == kBF16 && a.q_dtype == kBF16)
-    return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP, RT, ST, BAL>, grid, p, s);
-  if (a.kv_dtype == kF16 && a.q_dtype == kF16)
-    return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP, RT, ST, BAL>, grid, p, s);
-  if (a.kv_dtype == kFP8 && a.q_dtype == kBF16)
-    return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP, RT, ST, BAL>, grid, p, s);
-  if (a.kv_dtype == kFP8 && a.q_dtype == kF16)
-    return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP, RT, ST, BAL>, grid, p, s);
-  return hipErrorInvalidValue;
+  if constexpr (!BAL) {
+    if (p.lpt_shift >= 0) return dispatch_mfma_types<D, MT, AP, RT, ST, false, true>(a, grid, p, s);
+  }
+  return dispatch_mfma_types<D, MT, AP, RT, ST, BAL, false>(a, grid, p, s);
 }
 
 template <int D>
