@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("db4bb28b08e47b9496e21f29381e4f2a44f4f0c034cd948399178c7471cad3a5", "gqa70b-bf16-47x825-step", 1): 163112346,
-    ("db4bb28b08e47b9496e21f29381e4f2a44f4f0c034cd948399178c7471cad3a5", "gqa70b-bf16-47x825", 1): 162693120,
-    ("db4bb28b08e47b9496e21f29381e4f2a44f4f0c034cd948399178c7471cad3a5", "gqa70b-bf16-47x825-multi4", 1): 169735270,
+    ("708d48d413c9930930c2c977e5e2cbdbde93a43cbba32215e4b8199d8ed98517", "gqa70b-bf16-47x825-step", 1): 161767834,
+    ("708d48d413c9930930c2c977e5e2cbdbde93a43cbba32215e4b8199d8ed98517", "gqa70b-bf16-47x825", 1): 161369088,
+    ("708d48d413c9930930c2c977e5e2cbdbde93a43cbba32215e4b8199d8ed98517", "gqa70b-bf16-47x825-multi4", 1): 168387891,
 }
 
 

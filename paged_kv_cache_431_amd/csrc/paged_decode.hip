@@ -31,7 +31,8 @@
 //   flight.  Loads are issued unconditionally, so the compiler can wait for
 //   exactly the oldest tile instead of draining every outstanding load.  With
 //   16-bit caches each tile's loads go through a buffer resource sized to the
-//   tile, and a ring step past the wave's last tile gets a resource of size
+//   tile's rows inside the context (the tail slots of a last block are not
+//   read), and a ring step past the wave's last tile gets a resource of size
 //   0, whose loads return zeros without a memory access; with FP8 caches such
 //   a step re-reads the last tile.  Either way it computes nothing.  When one
 //   workgroup is the only reader of a (sequence, KV head)'s K/V (decode, and
@@ -1104,7 +1105,9 @@ decode_mfma_kernel(Params p) {
         const int sub = (t0 + j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
         const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
         if constexpr (KV != kFP8) {
-          const int bytes = ok && jr < cn ? kTileTokens * ROW : 0;
+          // the rows inside the context only: the unused tail slots of a
+          // sequence's last block come back as zeros without being read
+          const int bytes = ok && jr < cn ? r.lim * ROW : 0;
           const __amdgpu_buffer_rsrc_t kr =
               __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k_head + off), (short)0, bytes, kBufferWord3);
           const __amdgpu_buffer_rsrc_t vr =

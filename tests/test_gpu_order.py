@@ -83,12 +83,13 @@ def check_order_multi(wl, ms):
     assert_close(ordered, c.oracle_multi(q, qs), wl.kv_dtype, label=f"{wl.name} multi splits={n}")
 
 
-@pytest.mark.parametrize("group,tokens", [(4, 4), (8, 4), (8, 1)], ids=lambda x: str(x))
+@pytest.mark.parametrize("group,tokens", [(4, 4), (8, 4), (8, 1), (8, 8)], ids=lambda x: str(x))
 def test_multi_token_longest_first(group, tokens):
     """Speculative steps over 260 mixed-length sequences: one row tile per
-    unit (4 x 4 rows), two row tiles held by one workgroup (8 x 4 rows), and
-    one token (decode rows through the multi-token kernel).  Some sequences
-    have fewer cached tokens than new ones."""
+    unit (4 x 4 rows), two row tiles held by one workgroup (8 x 4 rows), one
+    token (decode rows through the multi-token kernel), and two row groups
+    per unit (8 x 8 rows).  Some sequences have fewer cached tokens than new
+    ones."""
     rng = np.random.default_rng(4312 + group + tokens)
     lens = rng.integers(1, 500, size=260, endpoint=True)
     lens[:4] = (1, 2, 3, 17)
