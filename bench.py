@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("708d48d413c9930930c2c977e5e2cbdbde93a43cbba32215e4b8199d8ed98517", "gqa70b-bf16-47x825-step", 1): 161767834,
-    ("708d48d413c9930930c2c977e5e2cbdbde93a43cbba32215e4b8199d8ed98517", "gqa70b-bf16-47x825", 1): 161369088,
-    ("708d48d413c9930930c2c977e5e2cbdbde93a43cbba32215e4b8199d8ed98517", "gqa70b-bf16-47x825-multi4", 1): 168387891,
+    ("9aa1cb84470783a06af79d1935bb3347465acd5a8136bec81a156edaa1f61a56", "gqa70b-bf16-47x825-step", 1): 161759642,
+    ("9aa1cb84470783a06af79d1935bb3347465acd5a8136bec81a156edaa1f61a56", "gqa70b-bf16-47x825", 1): 161374208,
+    ("9aa1cb84470783a06af79d1935bb3347465acd5a8136bec81a156edaa1f61a56", "gqa70b-bf16-47x825-multi4", 1): 168396800,
 }
 
 

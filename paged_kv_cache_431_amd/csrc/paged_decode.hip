@@ -29,12 +29,11 @@
 //   per lane, then streams the tiles through a ring of NBUF register buffers:
 //   while tile i is computed, the loads of the next NBUF-1 tiles are in
 //   flight.  Loads are issued unconditionally, so the compiler can wait for
-//   exactly the oldest tile instead of draining every outstanding load.  With
-//   16-bit caches each tile's loads go through a buffer resource sized to the
-//   tile's rows inside the context (the tail slots of a last block are not
-//   read), and a ring step past the wave's last tile gets a resource of size
-//   0, whose loads return zeros without a memory access; with FP8 caches such
-//   a step re-reads the last tile.  Either way it computes nothing.  When one
+//   exactly the oldest tile instead of draining every outstanding load.  Each
+//   tile's loads go through a buffer resource sized to the tile's rows
+//   inside the context (the tail slots of a last block are not read), and a
+//   ring step past the wave's last tile gets a resource of size 0, whose
+//   loads return zeros without a memory access: it computes nothing.  When one
 //   workgroup is the only reader of a (sequence, KV head)'s K/V (decode, and
 //   several query tokens held by one row group) the loads are non-temporal:
 //   nothing re-reads them.
@@ -647,13 +646,12 @@ __device__ __forceinline__ uint32_t fp8x2_to_pair(uint32_t w) {
   }
 }
 
-// 16-bit K/V loads go through a buffer resource per tile: its base is the
-// tile's address (wave-uniform), its size the tile's bytes, or 0 for a ring
-// step past the wave's last tile or a block id outside the pool, whose loads
-// then return zeros without touching memory (the hardware's range check), so
-// the ring issues every load unconditionally and reads no byte twice.  FP8
-// tiles (half the bytes, so twice the tiles per byte) measured faster with
-// plain loads, a step past the end re-reading the last tile.  When one
+// K/V loads go through a buffer resource per tile: its base is the tile's
+// address (wave-uniform), its size the bytes of the tile's rows inside the
+// context, or 0 for a ring step past the wave's last tile or a block id
+// outside the pool, whose loads then return zeros without touching memory
+// (the hardware's range check), so the ring issues every load
+// unconditionally and reads no byte twice.  When one
 // workgroup is the only reader of a (sequence, KV head)'s K/V, as in decode,
 // the loads are non-temporal (the caches do not keep the lines for a reuse
 // that never comes); when several workgroups (row groups of several query
@@ -662,15 +660,6 @@ __device__ __forceinline__ uint32_t fp8x2_to_pair(uint32_t w) {
 // vector register, the part common to the wave a scalar one.
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) 32-bit data format
 
-template <bool STREAM, class T>
-__device__ __forceinline__ T kv_gload(const uint8_t* p) {
-  if constexpr (STREAM) {
-    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
-  } else {
-    return *reinterpret_cast<const T*>(p);
-  }
-}
-
 template <bool STREAM>
 __device__ __forceinline__ u32x4 kv_load16(__amdgpu_buffer_rsrc_t r, int lane_off, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, STREAM ? 2 : 0));
@@ -678,6 +667,10 @@ __device__ __forceinline__ u32x4 kv_load16(__amdgpu_buffer_rsrc_t r, int lane_of
 template <bool STREAM>
 __device__ __forceinline__ u32x2 kv_load8(__amdgpu_buffer_rsrc_t r, int lane_off, int off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, off, STREAM ? 2 : 0));
+}
+template <bool STREAM>
+__device__ __forceinline__ uint32_t kv_load4(__amdgpu_buffer_rsrc_t r, int lane_off, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, off, STREAM ? 2 : 0);
 }
 
 template <int KV, int D>
@@ -1104,44 +1097,29 @@ decode_mfma_kernel(Params p) {
         r.tok0 = tok0;
         const int sub = (t0 + j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
         const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
-        if constexpr (KV != kFP8) {
-          // the rows inside the context only: the unused tail slots of a
-          // sequence's last block come back as zeros without being read
-          const int bytes = ok && jr < cn ? r.lim * ROW : 0;
-          const __amdgpu_buffer_rsrc_t kr =
-              __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k_head + off), (short)0, bytes, kBufferWord3);
-          const __amdgpu_buffer_rsrc_t vr =
-              __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(v_head + off), (short)0, bytes, kBufferWord3);
+        // the rows inside the context only: the unused tail slots of a
+        // sequence's last block come back as zeros without being read
+        const int bytes = ok && jr < cn ? r.lim * ROW : 0;
+        const __amdgpu_buffer_rsrc_t kr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k_head + off), (short)0, bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t vr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(v_head + off), (short)0, bytes, kBufferWord3);
 #pragma unroll
-          for (int c = 0; c < KCH; ++c) r.k[c] = kv_load16<STREAM>(kr, k_lane, c * 1024);
+        for (int c = 0; c < KCH; ++c) r.k[c] = kv_load16<STREAM>(kr, k_lane, c * 1024);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            if constexpr (VDW == 4) {
-              const u32x4 x = kv_load16<STREAM>(vr, v_lane, rr * ROW);
-              r.v[rr][0] = x[0];
-              r.v[rr][1] = x[1];
-              r.v[rr][2] = x[2];
-              r.v[rr][3] = x[3];
-            } else {
-              const u32x2 x = kv_load8<STREAM>(vr, v_lane, rr * ROW);
-              r.v[rr][0] = x[0];
-              r.v[rr][1] = x[1];
-            }
-          }
-        } else {
-          const uint8_t* kp = k_head + off + k_lane;
-#pragma unroll
-          for (int c = 0; c < KCH; ++c) r.k[c] = kv_gload<STREAM, u32x4>(kp + c * 1024);
-          const uint8_t* vp = v_head + off + v_lane;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            if constexpr (VDW == 2) {
-              const u32x2 x = kv_gload<STREAM, u32x2>(vp + rr * ROW);
-              r.v[rr][0] = x[0];
-              r.v[rr][1] = x[1];
-            } else {
-              r.v[rr][0] = kv_gload<STREAM, uint32_t>(vp + rr * ROW);
-            }
+        for (int rr = 0; rr < 4; ++rr) {
+          if constexpr (VDW == 4) {
+            const u32x4 x = kv_load16<STREAM>(vr, v_lane, rr * ROW);
+            r.v[rr][0] = x[0];
+            r.v[rr][1] = x[1];
+            r.v[rr][2] = x[2];
+            r.v[rr][3] = x[3];
+          } else if constexpr (VDW == 2) {
+            const u32x2 x = kv_load8<STREAM>(vr, v_lane, rr * ROW);
+            r.v[rr][0] = x[0];
+            r.v[rr][1] = x[1];
+          } else {
+            r.v[rr][0] = kv_load4<STREAM>(vr, v_lane, rr * ROW);
           }
         }
       };
