@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("9aa1cb84470783a06af79d1935bb3347465acd5a8136bec81a156edaa1f61a56", "gqa70b-bf16-47x825-step", 1): 161759642,
-    ("9aa1cb84470783a06af79d1935bb3347465acd5a8136bec81a156edaa1f61a56", "gqa70b-bf16-47x825", 1): 161374208,
-    ("9aa1cb84470783a06af79d1935bb3347465acd5a8136bec81a156edaa1f61a56", "gqa70b-bf16-47x825-multi4", 1): 168396800,
+    ("60ffb3ef59576a7734d9efc563304b1a43f3762e8090bd681ce4d28b0c47fa46", "gqa70b-bf16-47x825-step", 1): 161754522,
+    ("60ffb3ef59576a7734d9efc563304b1a43f3762e8090bd681ce4d28b0c47fa46", "gqa70b-bf16-47x825", 1): 161361920,
+    ("60ffb3ef59576a7734d9efc563304b1a43f3762e8090bd681ce4d28b0c47fa46", "gqa70b-bf16-47x825-multi4", 1): 168391680,
 }
 
 

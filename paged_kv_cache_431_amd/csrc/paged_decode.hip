@@ -365,6 +365,28 @@ __device__ __forceinline__ void store_out(const Params& p, size_t row, int chunk
   }
 }
 
+// Store DW outputs of one output row, elements c + 16 e (times `mul`): the
+// layout the cross-range merge works in, where each store instruction of a
+// row's 16 threads covers contiguous bytes.  Rounding as in store_out.
+template <int D>
+__device__ __forceinline__ void store_out_spread(const Params& p, size_t row, int c, const float* a, float mul) {
+  constexpr int DW = D / 16;
+  const size_t off = row * D + c;
+  if (p.out_dtype == kF32) {
+    float* o = static_cast<float*>(p.out) + off;
+#pragma unroll
+    for (int e = 0; e < DW; ++e) o[16 * e] = a[e] * mul;
+  } else {
+    uint16_t* o = static_cast<uint16_t*>(p.out) + off;
+#pragma unroll
+    for (int e = 0; e < DW; ++e) {
+      float y = a[e] * mul;
+      asm volatile("" : "+v"(y));
+      o[16 * e] = (uint16_t)(p.out_dtype == kBF16 ? f32_to_bf16_rne(y) : f32_to_f16_bits(y));
+    }
+  }
+}
+
 // Output row of row r (0..15) of row tile k of an item, false if the row
 // holds no query: decode rows are the group's query heads; with several query
 // tokens row r of tile k is (query token, head) = divmod(16 (rt + k) + r, group).
@@ -409,6 +431,13 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
   const int cidx = it.unit * RT + k;
   size_t row;
   const bool row_ok = out_row<MT>(p, it, k, g, row);
+  // This thread's elements of the row: chunk * DW + e with one range (16-byte
+  // output stores), chunk + 16 e for partial states, so that every store and
+  // load instruction of the merge covers 64 contiguous bytes of a row
+  // instead of scattering 4-byte accesses 32 bytes apart.
+  const bool whole = it.n_splits_seq == 1;
+  const int e0 = whole ? chunk * DW : chunk;
+  const int es = whole ? 1 : 16;
   float a[DW];
   float mstar = kNegInf, lstar = 0.f;
 #pragma unroll
@@ -421,12 +450,12 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
       const float f = mstar == kNegInf ? 0.f : fast_exp2(sm.m[w][g] - mstar);
       lstar += f * sm.l[w][g];
 #pragma unroll
-      for (int e = 0; e < DW; ++e) a[e] += f * sm.acc[w][g][chunk * DW + e];
+      for (int e = 0; e < DW; ++e) a[e] += f * sm.acc[w][g][e0 + es * e];
     }
   }
   // a row that sees no position (only with several query tokens, when a
   // sequence has more new tokens than cached ones) gets 0
-  if (it.n_splits_seq == 1) {
+  if (whole) {
     if (row_ok) store_out<D>(p, row, chunk, a, lstar > 0.f ? p.v_scale / lstar : 0.f);
     return;
   }
@@ -445,9 +474,9 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
   };
   if (row_ok) {
     const size_t prow = prow_of(it.split);
-    float* dst = p.ws_acc + prow * D + chunk * DW;
+    float* dst = p.ws_acc + prow * D + chunk;
 #pragma unroll
-    for (int e = 0; e < DW; ++e) store_agent(dst + e, a[e]);
+    for (int e = 0; e < DW; ++e) store_agent(dst + 16 * e, a[e]);
     if (chunk == 0) {
       store_agent(p.ws_ml + 2 * prow, mstar);
       store_agent(p.ws_ml + 2 * prow + 1, lstar);
@@ -476,11 +505,11 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
     const float l_i = load_agent(p.ws_ml + 2 * prow + 1);
     const float f = mm == kNegInf ? 0.f : fast_exp2(m_i - mm);
     ll += f * l_i;
-    const float* src = p.ws_acc + prow * D + chunk * DW;
+    const float* src = p.ws_acc + prow * D + chunk;
 #pragma unroll
-    for (int e = 0; e < DW; ++e) o[e] += f * load_agent(src + e);
+    for (int e = 0; e < DW; ++e) o[e] += f * load_agent(src + 16 * e);
   }
-  store_out<D>(p, row, chunk, o, ll > 0.f ? p.v_scale / ll : 0.f);
+  store_out_spread<D>(p, row, chunk, o, ll > 0.f ? p.v_scale / ll : 0.f);
 }
 
 // Balanced ranges (decode with long contexts over few (sequence, KV head)
