@@ -25,6 +25,9 @@ constexpr int kComputeUnits = 256;
 // most this many sequences, ranked by tile count in this many bins (LDS).
 constexpr int kLptMaxSeqs = 1024;
 constexpr int kLptBins = 2048;
+static_assert(kLptMaxSeqs % kDecodeThreads == 0 && kLptBins % kDecodeThreads == 0,
+              "the ranking gives every thread the same number of sequences and bins");
+static_assert(kDecodeWaves <= 4, "the ranking's workgroup scan keeps one partial per wave in 4 LDS slots");
 
 struct DecodeLaunch {
   void* out;
