@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("60ffb3ef59576a7734d9efc563304b1a43f3762e8090bd681ce4d28b0c47fa46", "gqa70b-bf16-47x825-step", 1): 161754522,
-    ("60ffb3ef59576a7734d9efc563304b1a43f3762e8090bd681ce4d28b0c47fa46", "gqa70b-bf16-47x825", 1): 161361920,
-    ("60ffb3ef59576a7734d9efc563304b1a43f3762e8090bd681ce4d28b0c47fa46", "gqa70b-bf16-47x825-multi4", 1): 168391680,
+    ("7e0b708a24d95ea88b48feedb7b20c65a4cf436b4aaa3977832e8b246a50912e", "gqa70b-bf16-47x825-step", 1): 161755546,
+    ("7e0b708a24d95ea88b48feedb7b20c65a4cf436b4aaa3977832e8b246a50912e", "gqa70b-bf16-47x825", 1): 161376256,
+    ("7e0b708a24d95ea88b48feedb7b20c65a4cf436b4aaa3977832e8b246a50912e", "gqa70b-bf16-47x825-multi4", 1): 168391885,
 }
 
 

@@ -1083,8 +1083,8 @@ decode_mfma_kernel(Params p) {
       // Decode step: every wave loads its (sequence, KV head)'s new K and V rows
       // right after the chunk's block ids, so waiting for the ids (L2-resident)
       // never waits for these (cold) rows, and before the chunk's first tile,
-      // whose loads they arrive with; the wave that owns the last position uses
-      // them (a wave with several chunks loads them again, 512 bytes a chunk).
+      // whose loads they arrive with; only the wave that owns the last
+      // position reads them, in its first chunk (the others' loads read nothing).
       // Lane l < CH holds 8 elements of K, lane CH + l those of V (the rest
       // none).  The loads are unconditional, whatever the element type (a
       // branch here would make the compiler drain every load in flight, and so
@@ -1102,10 +1102,14 @@ decode_mfma_kernel(Params p) {
         const int row = __builtin_amdgcn_readfirstlane((it.s * p.h_kv + it.kvh) * D * es);
         const int off_k = lane < CH ? row + lane * 8 * es : bytes;
         const int off_v = lane >= CH && lane < 2 * CH ? row + (lane - CH) * 8 * es : bytes;
+        // only the owner uses the rows, staging them during its first chunk:
+        // every other wave and chunk issues the same loads over resources of
+        // size 0, which read nothing (the same instructions keep the same waits)
+        const int avail = owner && c0 == 0 ? bytes : 0;
         const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_k), (short)0, bytes, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_k), (short)0, avail, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_v), (short)0, bytes, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_v), (short)0, avail, kBufferWord3);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           kx[w] = kv_load8<false>(rk, off_k, 8 * w);
