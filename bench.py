@@ -58,9 +58,9 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("7e0b708a24d95ea88b48feedb7b20c65a4cf436b4aaa3977832e8b246a50912e", "gqa70b-bf16-47x825-step", 1): 161755546,
-    ("7e0b708a24d95ea88b48feedb7b20c65a4cf436b4aaa3977832e8b246a50912e", "gqa70b-bf16-47x825", 1): 161376256,
-    ("7e0b708a24d95ea88b48feedb7b20c65a4cf436b4aaa3977832e8b246a50912e", "gqa70b-bf16-47x825-multi4", 1): 168391885,
+    ("a3de61d715dec28fb21fec9071a31c4f7435321222906f065e42ad1661bf217a", "gqa70b-bf16-47x825-step", 1): 161759642,
+    ("a3de61d715dec28fb21fec9071a31c4f7435321222906f065e42ad1661bf217a", "gqa70b-bf16-47x825", 1): 161376256,
+    ("a3de61d715dec28fb21fec9071a31c4f7435321222906f065e42ad1661bf217a", "gqa70b-bf16-47x825-multi4", 1): 168386765,
 }
 
 

@@ -186,7 +186,13 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   const int row_tiles = multi ? pkv::multi_row_tiles(h_q, h_kv, max_query_len) : 1;
   const int row_groups = multi ? pkv::multi_row_groups(row_tiles) : 1;
   if ((int64_t)ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_groups * n > INT32_MAX) return PKV_EUNSUPPORTED;
-  const int balanced = !multi && matrix_core ? balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits) : 0;
+  int balanced = !multi && matrix_core ? balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits) : 0;
+  // balanced ranges count every pair's tiles up to the table's capacity in an
+  // int (a context may exceed max_context_len); otherwise one workgroup per
+  // pair and split, whose layout the workspace size also covers
+  if (balanced > 0 && (int64_t)num_seqs * h_kv *
+                              ceil_div((int64_t)max_blocks_per_seq * block_size, pkv::kTileTokens) >= INT32_MAX)
+    balanced = 0;
   const pkv::WorkspaceLayout L = multi ? pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n)
                                        : pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n, balanced);
   if (workspace_bytes < L.total) return PKV_EWORKSPACE;
@@ -227,7 +233,6 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   a.k_scale_enc = k_scale;
   a.v_scale_enc = v_scale;
   a.balanced_workgroups = balanced;
-  a.max_context_len = max_context_len;
   // resident workgroups per SIMD: 2 for the kernels holding two row tiles
   const int waves_per_simd =
       multi && pkv::multi_tiles_per_workgroup(row_tiles) == 2 ? 2 : pkv::kDecodeWavesPerSimd;

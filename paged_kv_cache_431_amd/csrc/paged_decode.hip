@@ -124,7 +124,6 @@ struct Params {
   int num_query_tokens, max_query_len;
   int lpt_shift;   // decode: >= 0 takes sequences longest first (tile counts >> lpt_shift), -1 in order
   int balanced;    // decode: tiles of all (sequence, KV head) pairs cut into gridDim.x equal ranges
-  int max_ctx;     // balanced ranges: context lengths are taken at most this
   int row_tiles;   // 16-row tiles of (query token, head) rows per (sequence, KV head)
   int row_groups;  // workgroups per (sequence, KV head, split): row_tiles / RT, rounded up
   // Decode step that appends each sequence's new token itself (null
@@ -531,8 +530,9 @@ struct Balanced {
 __device__ void balanced_setup(const Params& p, int* pre, Balanced& b) {
   b.S = p.units / p.h_kv;
   b.H = p.h_kv;
-  // the host bounds all pairs' tiles at max_context_len each within int
-  b.cap = min(p.max_blocks_per_seq * p.block_size, p.max_ctx);
+  // contexts are clamped to the table's capacity, as items clamp them; the
+  // host keeps all pairs' tiles at that capacity within an int
+  b.cap = p.max_blocks_per_seq * p.block_size;
   const int S = b.S, cap = b.cap;
   auto seq_tiles = [&](int s) {
     int c = p.context_lens[s];
@@ -1458,7 +1458,6 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.row_groups = multi ? multi_row_groups(row_tiles) : 1;
   p.balanced = a.balanced_workgroups > 0 ? 1 : 0;
   p.lpt_shift = a.lpt_shift;
-  p.max_ctx = a.max_context_len;
   p.new_k = static_cast<const uint8_t*>(a.new_k);
   p.new_v = static_cast<const uint8_t*>(a.new_v);
   p.k_store = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));

@@ -61,9 +61,8 @@ struct DecodeLaunch {
   float k_scale_enc, v_scale_enc;
   // Balanced ranges (decode only, matrix-core path; 0 = one workgroup per
   // (sequence, KV head, split)): the grid, every workgroup one equal range of
-  // all pairs' tiles; context lengths are taken at most max_context_len.
+  // all pairs' tiles.
   int balanced_workgroups;
-  int max_context_len;
   // Longest pairs first (decode, one workgroup per (sequence, KV head,
   // split)): -1 = workgroups take pairs in (sequence, KV head) order; else
   // sequences are taken in decreasing order of their tile count shifted

@@ -8,7 +8,8 @@ workgroup) against the float64 oracle, through the C ABI:
     by decode, and the same pools;
   * 512 sequences of one KV head each (the most pairs the mode takes), so
     the prefix of tile counts spans many lanes;
-  * repeated calls reuse the workspace (its counters return to zero).
+  * repeated calls reuse the workspace (its counters return to zero);
+  * contexts longer than max_context_len are attended over in full.
 """
 
 import numpy as np
@@ -90,3 +91,24 @@ def test_most_pairs_the_balanced_mode_takes():
     assert_close(out, c.oracle_decode(seqs=seqs), wl.kv_dtype, seqs=seqs, label=wl.name)
     assert torch.isfinite(out).all()
     assert torch.count_nonzero(out[1]) == 0, "a sequence with no context must get zeros"
+
+
+def test_contexts_beyond_max_context_len_are_exact():
+    """max_context_len only sizes the assignment: sequences longer than it
+    (within their block tables) are still attended over in full, with
+    balanced ranges as with one workgroup per pair and split."""
+    wl = _wl("balanced-long-tail", (9000, 300, 4500, 0, 12000, 17), seed=99)
+    c = Case(wl)
+    c.scatter()
+    ref = c.oracle_decode()
+    short = 5000  # still long enough for balanced ranges (313 tiles)
+    assert c.plan.max_context_len > short
+    for splits in (0, 2):
+        print(f"[case] {wl.name} max_context_len={short} splits={splits}", flush=True)
+        ws = pkv.make_workspace(wl.num_seqs, wl.h_q, wl.h_kv, wl.head_dim, wl.block_size, short, splits)
+        out = torch.empty((wl.num_seqs, wl.h_q, wl.head_dim), dtype=torch.float32, device="cuda")
+        pkv.pkv_paged_attention_decode(out, c.t.q, c.t.k_cache, c.t.v_cache, c.block_tables, c.context_lens,
+                                       max_context_len=short, k_scale=c.t.k_scale, v_scale=c.t.v_scale,
+                                       num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out, ref, wl.kv_dtype, label=f"{wl.name}-splits{splits}")
