@@ -1,0 +1,76 @@
+"""Edge cases of the boundary on the GPU, through the C ABI:
+
+  * calls with nothing to do (no sequence, no token) succeed, launch nothing
+    and leave every buffer as it was;
+  * the scatter skips every slot outside the pool (a negative slot marks a
+    padding token) and writes the others exactly as the oracle's scatter of
+    the in-range tokens alone does, bit for bit over the whole pool.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.scatter
+import paged_kv_cache_431_amd as pkv
+import workloads
+from pkv_cases import Case, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(kv):
+    q = "bf16" if kv in ("bf16", "fp8") else kv
+    wl = workloads.Workload(f"edges-{kv}", 6, 8, 2, 64, 16, q, kv, q, 71, contexts=(0, 1, 17, 40, 16, 33),
+                            extra_blocks=3)
+    return Case(wl)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32", "fp8"])
+def test_empty_calls_touch_nothing(kv):
+    c = _case(kv)
+    wl = c.wl
+    print(f"[case] {wl.name} empty calls", flush=True)
+    k0, v0 = to_bits(c.t.k_cache).copy(), to_bits(c.t.v_cache).copy()
+    mb = c.block_tables.shape[1]
+    q0 = torch.empty((0, wl.h_q, wl.head_dim), dtype=c.t.q.dtype, device="cuda")
+    out0 = torch.empty((0, wl.h_q, wl.head_dim), dtype=torch.float32, device="cuda")
+    bt0 = torch.empty((0, mb), dtype=torch.int32, device="cuda")
+    cl0 = torch.empty((0,), dtype=torch.int32, device="cuda")
+    new0 = torch.empty((0, wl.h_kv, wl.head_dim), dtype=c.t.new_k.dtype, device="cuda")
+    slots0 = torch.empty((0,), dtype=torch.int64, device="cuda")
+    kw = dict(k_scale=c.t.k_scale, v_scale=c.t.v_scale)
+    pkv.pkv_paged_attention_decode(out0, q0, c.t.k_cache, c.t.v_cache, bt0, cl0,
+                                   max_context_len=c.plan.max_context_len, **kw)
+    pkv.pkv_reshape_and_cache(new0, new0, c.t.k_cache, c.t.v_cache, slots0, **kw)
+    if kv != "f32":  # the one-launch step exists for the matrix-core caches
+        pkv.pkv_decode_step(out0, q0, new0, new0, c.t.k_cache, c.t.v_cache, bt0, cl0,
+                            max_context_len=c.plan.max_context_len, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(c.t.k_cache), k0), "an empty call changed the K pool"
+    assert np.array_equal(to_bits(c.t.v_cache), v0), "an empty call changed the V pool"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32", "fp8"])
+def test_scatter_skips_slots_outside_the_pool(kv):
+    c = _case(kv)
+    wl = c.wl
+    nb, bs = c.t.k_cache.shape[0], wl.block_size
+    rng = np.random.default_rng(72)
+    slots = rng.choice(nb * bs, size=wl.num_seqs, replace=False).astype(np.int64)
+    slots[1] = -1                # padding
+    slots[3] = nb * bs           # one past the pool
+    slots[4] = nb * bs + 12345
+    slots[5] = -(1 << 40)
+    print(f"[case] {wl.name} slots {slots.tolist()}", flush=True)
+    k0, v0 = to_bits(c.t.k_cache).copy(), to_bits(c.t.v_cache).copy()
+    pkv.pkv_reshape_and_cache(c.t.new_k, c.t.new_v, c.t.k_cache, c.t.v_cache, torch.from_numpy(slots).cuda(),
+                              k_scale=c.t.k_scale, v_scale=c.t.v_scale)
+    torch.cuda.synchronize()
+    keep = (slots >= 0) & (slots < nb * bs)
+    assert keep.sum() == 2
+    ek, ev = oracle.scatter.reshape_and_cache(
+        to_bits(c.t.new_k)[keep], to_bits(c.t.new_v)[keep], k0.copy(), v0.copy(), slots[keep],
+        in_dtype=wl.new_dtype, kv_dtype=wl.kv_dtype, block_size=bs, k_scale=c.t.k_scale, v_scale=c.t.v_scale)
+    assert np.array_equal(to_bits(c.t.k_cache), ek), "K pool differs from the oracle's scatter of the in-range slots"
+    assert np.array_equal(to_bits(c.t.v_cache), ev), "V pool differs from the oracle's scatter of the in-range slots"
