@@ -4,7 +4,9 @@
     and leave every buffer as it was;
   * the scatter skips every slot outside the pool (a negative slot marks a
     padding token) and writes the others exactly as the oracle's scatter of
-    the in-range tokens alone does, bit for bit over the whole pool.
+    the in-range tokens alone does, bit for bit over the whole pool;
+  * block ids outside the pool and context lengths outside the table are
+    kept inside their own sequence: the others keep their bits.
 """
 
 import numpy as np
@@ -74,3 +76,51 @@ def test_scatter_skips_slots_outside_the_pool(kv):
         in_dtype=wl.new_dtype, kv_dtype=wl.kv_dtype, block_size=bs, k_scale=c.t.k_scale, v_scale=c.t.v_scale)
     assert np.array_equal(to_bits(c.t.k_cache), ek), "K pool differs from the oracle's scatter of the in-range slots"
     assert np.array_equal(to_bits(c.t.v_cache), ev), "V pool differs from the oracle's scatter of the in-range slots"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_bad_device_data_stays_inside_its_sequence(kv):
+    """Block ids outside the pool are skipped, a negative context length is
+    taken as 0 and one beyond the table as the table's capacity: the call
+    completes, the sequences with valid data keep their bits, and the one
+    with a negative length gets zeros.  (What a sequence with bad ids
+    receives is unspecified.)"""
+    q = "bf16" if kv == "bf16" else kv
+    c = Case(workloads.Workload(f"edges-bad-{kv}", 8, 8, 2, 64, 16, q, kv, q, 73,
+                                contexts=(0, 1, 17, 40, 16, 33, 300, 77), extra_blocks=3))
+    wl = c.wl
+    good = [0, 1, 6, 7]
+    c.scatter()
+    clean = c.decode()
+    nb, mb = c.t.k_cache.shape[0], c.block_tables.shape[1]
+    bt = c.block_tables.clone()
+    lens = c.context_lens.clone()
+    bt[2, 0] = nb          # one past the pool
+    bt[3, 1] = -7
+    lens[4] = -5
+    lens[5] = mb * wl.block_size + 1000
+    print(f"[case] {wl.name} bad ids in sequences 2, 3; lengths {lens.tolist()}", flush=True)
+    out = torch.empty_like(clean)
+    pkv.pkv_paged_attention_decode(out, c.t.q, c.t.k_cache, c.t.v_cache, bt, lens,
+                                   max_context_len=c.plan.max_context_len, k_scale=c.t.k_scale, v_scale=c.t.v_scale)
+    torch.cuda.synchronize()
+    for s in good:
+        assert torch.equal(out[s], clean[s]), f"sequence {s} changed"
+    assert torch.count_nonzero(out[4]) == 0, "a negative context length must give zeros"
+    if kv != "f32":
+        print(f"[case] {wl.name} decode step with the same tables", flush=True)
+        k0, v0 = to_bits(c.t.k_cache).copy(), to_bits(c.t.v_cache).copy()
+        out2 = torch.empty_like(clean)
+        pkv.pkv_decode_step(out2, c.t.q, c.t.new_k, c.t.new_v, c.t.k_cache, c.t.v_cache, bt, lens,
+                            max_context_len=c.plan.max_context_len, k_scale=c.t.k_scale, v_scale=c.t.v_scale)
+        torch.cuda.synchronize()
+        for s in good:
+            assert torch.equal(out2[s], clean[s]), f"decode step: sequence {s} changed"
+        assert torch.count_nonzero(out2[4]) == 0
+        # the step rewrote the new tokens of the sequences with valid tables
+        # at the slots they already held: those pools bytes are unchanged
+        kb, vb = to_bits(c.t.k_cache), to_bits(c.t.v_cache)
+        valid_blocks = c.rp.block_tables[good].ravel()
+        valid_blocks = valid_blocks[(valid_blocks >= 0) & (valid_blocks < nb)]
+        assert np.array_equal(kb[valid_blocks], k0[valid_blocks])
+        assert np.array_equal(vb[valid_blocks], v0[valid_blocks])
