@@ -10,10 +10,11 @@ separate reshape_and_cache and decode calls for the same work).  Each layer has 
 
 value = KV bytes a step must read (sum over sequences of context_len x 2 x
 h_kv x head_dim x 2 B, x 80 layers) / step time, in GB/s.
-roofline = the step's attention kernel alone: the same bytes per launch / its mean
-launch duration (HIP events on its stream around back-to-back launches over
-the layer pools); traffic = HBM bytes per launch from rocprofv3 counters,
-reported only while the kernel source is the one they were taken on.
+roofline = the step's attention kernel: the same bytes per launch / its mean
+launch duration, which is the step time over 80 when the step is one launch
+per layer (HIP events on the kernel's stream around the timed loop);
+traffic = HBM bytes per launch from rocprofv3 counters, reported only while
+the kernel source is the one they were taken on.
 copy_blocks = the block copy of copy-on-write (1,024 block pairs, K and V).
 swap_blocks = preemption by swap: 1,024 scattered blocks (K and V) to pinned
 host memory and back in one launch each way, GB/s against PCIe 5.0 x16.
@@ -26,7 +27,8 @@ target); bytes_per_layer_call = the bytes a call moves besides the used K/V
 roofline.measured_stream_peaks = a 2 GiB device copy's read + write rate and
 a 2 GiB float32 sum's read rate (library kernels), beside the published 8 TB/s.
 cpu_baseline = the float64 oracle on whole layer calls, repeated for a
-bounded time on the host, with all its threads and then with one.
+bounded time on the host with its thread pools held to one thread (the
+one core it uses), and briefly with the default pools for comparison.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
 """
@@ -155,13 +157,18 @@ def stream_peaks(dev, nbytes, reps=10):
     return 2 * nbytes / (copy_ms * 1e-3) / 1e9, nbytes / (sum_ms * 1e-3) / 1e9
 
 
-def cpu_baseline(plan, rp, tensors, budget_s, one_thread_budget_s):
+def cpu_baseline(plan, rp, tensors, budget_s, blas_budget_s):
     """Time the oracle on whole layer calls of the workload (the scatter of the
     new tokens, then float64 attention one sequence at a time), repeating the
-    layer until about budget_s seconds of host work are done; then the same
-    with every thread pool held to one thread for one_thread_budget_s."""
+    layer until about budget_s seconds of host work are done, with every
+    thread pool held to one thread: the oracle walks one sequence and head at
+    a time through small float64 products, so one core is what it uses.  A
+    second run of blas_budget_s seconds leaves the BLAS and torch thread pools
+    at their defaults and reports their size beside the rate, which shows
+    that more threads do not speed it up."""
     import numpy as np
     import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle.attention
     import oracle.scatter
@@ -191,33 +198,31 @@ def cpu_baseline(plan, rp, tensors, budget_s, one_thread_budget_s):
             if time.perf_counter() - t0 > budget:
                 return done_calls, time.perf_counter() - t0
 
-    def threads_in_use():
-        try:
-            from threadpoolctl import threadpool_info
-            return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
-        except Exception:
-            return 1
+    def pool_threads():
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
 
     def sample(calls, dt):
         return (f"{calls} repeats of one layer call of {wl.name} ({wl.num_seqs} sequences: scatter of the new "
                 f"tokens, then float64 attention one sequence at a time), {dt:.1f} s")
 
-    calls, dt = run(budget_s)
-    result = {"value": round(calls * per_call / dt / 1e9, 4), "unit": "GB/s", "cores": threads_in_use(),
-              "kind": "oracle", "seqs_per_s": round(calls * wl.num_seqs / dt, 3), "host_cpus": os.cpu_count(),
-              "sample": sample(calls, dt)}
-    if one_thread_budget_s > 0:
-        from threadpoolctl import threadpool_limits
-        torch_threads = torch.get_num_threads()
-        with threadpool_limits(limits=1):
-            torch.set_num_threads(1)
-            try:
-                calls1, dt1 = run(one_thread_budget_s)
-                cores1 = threads_in_use()
-            finally:
-                torch.set_num_threads(torch_threads)
-        result["one_thread"] = {"value": round(calls1 * per_call / dt1 / 1e9, 4), "unit": "GB/s", "cores": cores1,
-                                "seqs_per_s": round(calls1 * wl.num_seqs / dt1, 3), "sample": sample(calls1, dt1)}
+    torch_threads = torch.get_num_threads()
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        try:
+            calls, dt = run(budget_s)
+            assert pool_threads() == 1
+        finally:
+            torch.set_num_threads(torch_threads)
+    result = {"value": round(calls * per_call / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+              "seqs_per_s": round(calls * wl.num_seqs / dt, 3), "host_cpus": os.cpu_count(),
+              "sample": sample(calls, dt) + ", every thread pool held to one thread"}
+    if blas_budget_s > 0:
+        calls2, dt2 = run(blas_budget_s)
+        result["default_thread_pools"] = {
+            "value": round(calls2 * per_call / dt2 / 1e9, 4), "unit": "GB/s", "blas_threads": pool_threads(),
+            "torch_threads": torch_threads, "sample": sample(calls2, dt2),
+            "note": "the same oracle with the BLAS and torch pools at their default sizes; its products are too "
+                    "small to spread over them, so it still runs on about one core"}
     return result
 
 
@@ -273,9 +278,10 @@ def main():
     ap.add_argument("--layers", type=int, default=80)
     ap.add_argument("--block-size", type=int, default=0, help="tokens per block (0: the workload's own, 16)")
     ap.add_argument("--splits", type=int, default=0, help="force the decode split count (0 = library's choice)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--cpu-budget-one-thread", type=float, default=10.0,
-                    help="seconds of oracle work held to one thread (0 skips that run)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for cpu_baseline (thread pools held to one thread)")
+    ap.add_argument("--cpu-budget-default-threads", type=float, default=5.0,
+                    help="seconds of oracle work with the default thread pools (0 skips that run)")
     ap.add_argument("--copy-peak-mib", type=int, default=2048,
                     help="buffer size of the copy and sum that measure streaming rates (0 skips them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -367,20 +373,25 @@ def main():
     ms_step = time_step(layer_calls)
     ms_two = time_step(two_launch_calls) if fused else ms_step
 
-    # The step's attention kernel alone: L back-to-back launches (one per
-    # layer pool) between one event pair on the kernel's stream, repeated;
-    # the mean launch duration is the total over the launches.  An event pair
-    # around each single launch is also kept (it adds the event and dispatch
-    # overhead).
+    # The step's attention kernel: where the step is one launch per layer
+    # (the decode step kernel), the timed step loop above is nothing but L
+    # back-to-back launches of it, so its mean launch duration is the step
+    # time over L (by construction never more than the step).  Otherwise the
+    # decode kernel alone is timed the same way in a loop of its own.  An
+    # event pair around each single launch is also kept (it adds the event
+    # and dispatch overhead).
     reps = max(1, min(5, args.steps))
-    batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in batch:
-        a.record(stream)
-        for call in kernel_calls:
-            call()
-        b.record(stream)
-    torch.cuda.synchronize()
-    mean_launch_ms = sum(a.elapsed_time(b) for a, b in batch) / (reps * L)
+    if fused:
+        mean_launch_ms = ms_step / L
+    else:
+        batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in batch:
+            a.record(stream)
+            for call in kernel_calls:
+                call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        mean_launch_ms = sum(a.elapsed_time(b) for a, b in batch) / (reps * L)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * L)]
     for r in range(reps):
         for l, call in enumerate(kernel_calls):
@@ -454,6 +465,8 @@ def main():
                      "kernel": ("decode_mfma_kernel (decode step, new tokens written in-kernel)" if fused else
                                 "decode_mfma_kernel" if wl.kv_dtype != "f32" else "decode_vector_kernel"),
                      "mean_launch_us": round(mean_launch_ms * 1e3, 3),
+                     "mean_launch_source": ("the timed step loop (ms_per_step / layers)" if fused else
+                                            "back-to-back decode launches over the layer pools"),
                      "isolated_launch_median_us": round(launch_ms[len(launch_ms) // 2] * 1e3, 3),
                      "isolated_launch_p10_us": round(pct(launch_ms, 0.1) * 1e3, 3),
                      "isolated_launch_p90_us": round(pct(launch_ms, 0.9) * 1e3, 3),
@@ -528,7 +541,7 @@ def main():
         del pools, decodes, scatters, layer_calls, multis, steps_fused, two_launch_calls, kernel_calls
         torch.cuda.empty_cache()
         fresh = workloads.make_tensors(plan, rp, device=dev, poison=False, pool_seed_offset=0)  # untouched by HIP
-        result["cpu_baseline"] = cpu_baseline(plan, rp, fresh, args.cpu_budget, args.cpu_budget_one_thread)
+        result["cpu_baseline"] = cpu_baseline(plan, rp, fresh, args.cpu_budget, args.cpu_budget_default_threads)
     print(json.dumps(result), flush=True)
 
 

@@ -43,6 +43,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -58,17 +60,18 @@ typedef enum {
 typedef enum {
   PKV_OK = 0,
   PKV_EINVAL = 1,        /* a scalar argument is out of range or a pointer is NULL */
-  PKV_EUNSUPPORTED = 2,  /* valid, but this dtype / head_dim / group combination is not built */
+  PKV_EUNSUPPORTED = 2,  /* valid, but this dtype / group / block-size combination is not built */
   PKV_ENOSPC = 3,        /* block manager: the pool cannot supply the blocks (state unchanged) */
-  PKV_EWORKSPACE = 4,    /* workspace smaller than pkv_decode_workspace_bytes() */
+  PKV_EWORKSPACE = 4,    /* workspace smaller than the sizing call returns */
   PKV_EHIP = 5           /* the HIP runtime reported an error at launch */
 } pkv_status;
 
-/* Human-readable name of a status code (static string). */
-const char* pkv_status_str(int status);
+/* Human-readable name of a status code (static string; "unknown ..." for
+ * a value outside the enum). */
+const char* pkv_status_str(pkv_status status);
 
 /* ABI version of this header (bumped on any signature change). */
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 int pkv_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -92,42 +95,68 @@ int pkv_abi_version(void);
  * h, t % B, :] (times k_scale for FP8) and likewise for V.  ctx_s = 0 gives 0.
  *
  * Supported combinations (others return PKV_EUNSUPPORTED):
- *   D in {64, 128}; 1 <= Hq / Hkv <= 16; B >= 1;
+ *   1 <= Hq / Hkv <= 16; B >= 1;
  *   (q, kv) in {(F32, F32), (F16, F16), (BF16, BF16), (BF16, FP8_E4M3),
  *   (F16, FP8_E4M3)}.  The matrix-core path serves the 16-bit and FP8 caches
- *   when B is a multiple of 16; everything else takes the vector path.
+ *   when B is 16 times a power of two; everything else takes the vector path.
+ *   D must be 64 or 128 (another D is PKV_EINVAL).
  *
  * max_context_len: an upper bound the host knows for max_s ctx_s (used only
  *   to size the split over blocks; a longer ctx_s is still computed exactly).
  * scale: logit scale; pass 0 (or a negative value) for 1/sqrt(D).
  * k_scale, v_scale: per-tensor FP8 scales (ignored for other kv dtypes).
- * num_splits: 0 lets the library choose how many workgroups share one
- *   sequence's blocks; a positive value forces that count (tests, tuning).
  *
- * Workspace: device memory of at least pkv_decode_workspace_bytes(...) bytes
- *   for the same (S, Hq, Hkv, D, max_context_len, num_splits).  It must be
- *   zero-filled before its FIRST use; every call leaves it ready for the next
- *   (its counters return to zero), so it is reused without clearing.  Two
- *   calls in flight at once must not share a workspace.
- *   Errors: PKV_EINVAL (NULL pointer, S < 0, Hq % Hkv != 0, B < 1,
- *   max_context_len > MB * B, ...), PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP.
+ * Workspace: device memory of at least
+ *   pkv_decode_workspace_bytes(S, Hq, D, max_context_len, B) bytes.  It must
+ *   be zero-filled before its FIRST use; every call leaves it ready for the
+ *   next (its counters return to zero), so it is reused without clearing.
+ *   Two calls in flight at once must not share a workspace.
+ * Errors: PKV_EINVAL (NULL pointer, S < 0, Hq % Hkv != 0, B < 1, D not in
+ *   {64, 128}, max_context_len > MB * B, ...), PKV_EUNSUPPORTED,
+ *   PKV_EWORKSPACE, PKV_EHIP.
  * ------------------------------------------------------------------------ */
-size_t pkv_decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
-                                  int max_context_len, int num_splits);
 
-/* The split count the library will use for these sizes (>= 1), or 0 if invalid. */
+/* Workspace bytes for any decode call (pkv_paged_attention_decode or
+ * pkv_decode_step) with these sizes and any h_kv that divides h_q, the
+ * library choosing the split count; 0 for invalid sizes. */
+size_t pkv_decode_workspace_bytes(int num_seqs, int h_q, int head_dim, int max_context_len, int block_size);
+
+pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
+                                      const void* q, pkv_dtype q_dtype,
+                                      const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                      float k_scale, float v_scale,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                                      int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                      float scale, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Split-count tuning (tests, sweeps): the same decode with a forced count of
+ * workgroups per (sequence, KV head).
+ *
+ * num_splits: 0 lets the library choose (exactly the calls above); a
+ *   positive value forces that count.
+ * pkv_decode_workspace_bytes_splits: the workspace such a call needs (h_kv
+ *   given); 0 for invalid sizes.
+ * pkv_decode_num_splits: the split count the library will use for these
+ *   sizes (>= 1), or 0 if invalid.
+ * ------------------------------------------------------------------------ */
+size_t pkv_decode_workspace_bytes_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                                         int max_context_len, int num_splits);
+
 int pkv_decode_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
                           int max_context_len, int num_splits);
 
-int pkv_paged_attention_decode(void* out, int out_dtype,
-                               const void* q, int q_dtype,
-                               const void* k_cache, const void* v_cache, int kv_dtype,
-                               float k_scale, float v_scale,
-                               const int32_t* block_tables, const int32_t* context_lens,
-                               int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
-                               int num_blocks, int max_blocks_per_seq, int max_context_len,
-                               float scale, int num_splits,
-                               void* workspace, size_t workspace_bytes, void* stream);
+pkv_status pkv_paged_attention_decode_splits(void* out, pkv_dtype out_dtype,
+                                             const void* q, pkv_dtype q_dtype,
+                                             const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                             float k_scale, float v_scale,
+                                             const int32_t* block_tables, const int32_t* context_lens,
+                                             int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                                             int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                             float scale, int num_splits,
+                                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * One decode step in one launch: each sequence's new token is written into
@@ -145,17 +174,32 @@ int pkv_paged_attention_decode(void* out, int out_dtype,
  *                 new_dtype == kv_dtype copies the bits; an FP8_E4M3 pool
  *                 takes F32 / F16 / BF16 with the scatter's rounding
  *                 (x / k_scale or x / v_scale).  A sequence with context
- *                 length 0 has no new token and gets output 0.
+ *                 length 0 has no new token and gets output 0.  A sequence
+ *                 whose context length exceeds MB * B (its table cannot hold
+ *                 the position) is attended over its MB * B cached tokens and
+ *                 its new token is not written.
  *   other arguments as for pkv_paged_attention_decode (same workspace).
  * Supported: the matrix-core combinations of decode, with new_k / new_v
  *   under 2 GiB each; others return PKV_EUNSUPPORTED (use the two calls).
  *   Errors as for decode, plus PKV_EINVAL for NULL new_k / new_v with S > 0.
+ * pkv_decode_step_splits forces the split count as
+ *   pkv_paged_attention_decode_splits does (its workspace sizing too).
  * ------------------------------------------------------------------------ */
-int pkv_decode_step(void* out, int out_dtype, const void* q, int q_dtype, const void* new_k, const void* new_v,
-                    int new_dtype, void* k_cache, void* v_cache, int kv_dtype, float k_scale, float v_scale,
-                    const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
-                    int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
-                    float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+pkv_status pkv_decode_step(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                           const void* new_k, const void* new_v, pkv_dtype new_dtype,
+                           void* k_cache, void* v_cache, pkv_dtype kv_dtype, float k_scale, float v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q,
+                           int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                           int max_context_len, float scale, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+pkv_status pkv_decode_step_splits(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                  const void* new_k, const void* new_v, pkv_dtype new_dtype,
+                                  void* k_cache, void* v_cache, pkv_dtype kv_dtype, float k_scale, float v_scale,
+                                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q,
+                                  int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                                  int max_context_len, float scale, int num_splits, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Paged attention for several new query tokens per sequence (a chunk of a
@@ -188,9 +232,10 @@ int pkv_decode_step(void* out, int out_dtype, const void* q, int q_dtype, const 
  * query_start[s] = s give exactly the decode call.
  *
  * Supported: the matrix-core combinations of decode (16-bit or FP8 caches,
- * B a multiple of 16 with B / 16 a power of two, D in {64, 128},
- * 1 <= Hq / Hkv <= 16); others return PKV_EUNSUPPORTED.  The (query token,
- * head) rows of one (sequence, KV head) are processed 16 at a time.
+ * B a multiple of 16 with B / 16 a power of two, 1 <= Hq / Hkv <= 16);
+ * others return PKV_EUNSUPPORTED.  D must be 64 or 128, as for decode.  The
+ * (query token, head) rows of one (sequence, KV head) are processed 16 at a
+ * time.
  * max_query_len: 1 <= max_query_len <= 2^24, an upper bound of every m_s.
  * Workspace: pkv_multi_workspace_bytes(...) bytes for the same sizes, zeroed
  *   before first use and reusable afterwards, as for decode.
@@ -204,12 +249,13 @@ size_t pkv_multi_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, 
 int pkv_multi_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
                          int max_context_len, int num_splits);
 
-int pkv_paged_attention_multi(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
-                              int num_query_tokens, int max_query_len, const void* k_cache, const void* v_cache,
-                              int kv_dtype, float k_scale, float v_scale, const int32_t* block_tables,
-                              const int32_t* context_lens, int num_seqs, int h_q, int h_kv, int head_dim,
-                              int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
-                              float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+pkv_status pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                     const int32_t* query_start, int num_query_tokens, int max_query_len,
+                                     const void* k_cache, const void* v_cache, pkv_dtype kv_dtype, float k_scale,
+                                     float v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                                     int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int num_blocks,
+                                     int max_blocks_per_seq, int max_context_len, float scale, int num_splits,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * reshape_and_cache: write each new token's K and V into its slot.
@@ -228,11 +274,11 @@ int pkv_paged_attention_multi(void* out, int out_dtype, const void* q, int q_dty
  *   one correctly rounded binary32 division, saturating to +-448, NaN -> 0x7F.
  * D must be a multiple of 8.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
  * ------------------------------------------------------------------------ */
-int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype,
-                          void* k_cache, void* v_cache, int kv_dtype,
-                          float k_scale, float v_scale,
-                          const int64_t* slot_mapping, int num_tokens,
-                          int h_kv, int head_dim, int block_size, int num_blocks, void* stream);
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype in_dtype,
+                                 void* k_cache, void* v_cache, pkv_dtype kv_dtype,
+                                 float k_scale, float v_scale,
+                                 const int64_t* slot_mapping, int num_tokens,
+                                 int h_kv, int head_dim, int block_size, int num_blocks, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * copy_blocks: the block copy of copy-on-write.
@@ -254,8 +300,9 @@ int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype,
  *                must be a multiple of 16.
  * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
  * ------------------------------------------------------------------------ */
-int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, const int32_t* block_pairs, int num_pairs,
-                    int h_kv, int head_dim, int block_size, int num_blocks, void* stream);
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype kv_dtype, const int32_t* block_pairs,
+                           int num_pairs, int h_kv, int head_dim, int block_size, int num_blocks,
+                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * swap_blocks: move whole blocks between two pools, typically a device pool
@@ -282,9 +329,9 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, const int32_t* b
  * has been synchronised.  h_kv * B * D * element bytes must be a multiple of
  * 16.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
  * ------------------------------------------------------------------------ */
-int pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* src_k, const void* src_v,
-                    int src_num_blocks, int kv_dtype, const int32_t* block_pairs, int num_pairs, int h_kv,
-                    int head_dim, int block_size, void* stream);
+pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* src_k, const void* src_v,
+                           int src_num_blocks, pkv_dtype kv_dtype, const int32_t* block_pairs, int num_pairs,
+                           int h_kv, int head_dim, int block_size, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Host block manager (no device memory; pure host bookkeeping)
@@ -307,7 +354,7 @@ typedef struct pkv_bm pkv_bm;
 
 /* Create a manager; *out receives it.  PKV_EINVAL on bad sizes or a
  * free_order that is not a permutation. */
-int pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pkv_bm** out);
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pkv_bm** out);
 void pkv_bm_destroy(pkv_bm* bm);
 
 /* Append n_tokens tokens to seq (created empty if new).  slots_out (may be
@@ -317,34 +364,34 @@ void pkv_bm_destroy(pkv_bm* bm);
  * the caller must copy the filled slots of src into dst; otherwise both are
  * -1.  PKV_ENOSPC if the pool cannot supply every block needed (nothing
  * changes); PKV_EINVAL for seq < 0 or n_tokens < 0. */
-int pkv_bm_append(pkv_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out,
-                  int32_t* cow_src, int32_t* cow_dst);
+pkv_status pkv_bm_append(pkv_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                         int32_t* cow_src, int32_t* cow_dst);
 
 /* child becomes a copy of parent sharing all its blocks (refcounts + 1).
  * PKV_EINVAL if parent is unknown or child exists. */
-int pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child);
+pkv_status pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child);
 
 /* Drop seq; blocks whose refcount reaches zero go to the back of the free
  * list in block-table order.  PKV_EINVAL if seq is unknown. */
-int pkv_bm_free(pkv_bm* bm, int32_t seq);
+pkv_status pkv_bm_free(pkv_bm* bm, int32_t seq);
 
 /* Copy seq's block table (up to cap entries) into out; *n_blocks and
  * *n_tokens receive its length in blocks and tokens.  PKV_EINVAL if unknown
  * or cap is too small. */
-int pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t cap,
-                       int32_t* n_blocks, int32_t* n_tokens);
+pkv_status pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t cap,
+                              int32_t* n_blocks, int32_t* n_tokens);
 
 /* Fill the device-bound metadata of a batch: tables [num_seqs, max_blocks]
  * (unused entries -1) and context_lens [num_seqs] for the listed sequences.
  * PKV_EINVAL if a sequence is unknown or longer than max_blocks blocks. */
-int pkv_bm_export(const pkv_bm* bm, const int32_t* seqs, int32_t num_seqs,
-                  int32_t* tables, int32_t max_blocks, int32_t* context_lens);
+pkv_status pkv_bm_export(const pkv_bm* bm, const int32_t* seqs, int32_t num_seqs,
+                         int32_t* tables, int32_t max_blocks, int32_t* context_lens);
 
 int32_t pkv_bm_num_free(const pkv_bm* bm);
 /* Reference count of a block (0 = free), or -1 for an id outside the pool. */
 int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
 /* Copy the free list, front first (up to cap entries); *n receives its length. */
-int pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+pkv_status pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n);
 
 #ifdef __cplusplus
 }

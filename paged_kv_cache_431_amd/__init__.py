@@ -15,7 +15,8 @@ HIP stream to the C ABI declared in include/pkv.h (same function names).
   pkv_reshape_and_cache        write new tokens' K/V into their slots
   pkv_copy_blocks              copy blocks (src -> dst) in both pools: copy-on-write
   pkv_swap_blocks              move blocks between a device pool and a pinned host pool
-  pkv_decode_workspace_bytes   workspace size for a decode call
+  pkv_decode_workspace_bytes   workspace size for a decode call (any h_kv, library's splits)
+  pkv_decode_workspace_bytes_splits  ... for a forced split count
   pkv_decode_num_splits        split count the library will use
   pkv_multi_workspace_bytes    workspace size for a call with several query tokens
   pkv_multi_num_splits         its split count
@@ -57,17 +58,25 @@ def lib():
     c_int, c_i32, c_sz, c_f, c_p = ctypes.c_int, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
     p_i32 = ctypes.POINTER(ctypes.c_int32)
     p_i64 = ctypes.POINTER(ctypes.c_int64)
+    # (out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+    #  block_tables, context_lens, S, Hq, Hkv, D, B, NB, MB, max_context_len,
+    #  scale, workspace, workspace_bytes, stream); the *_splits calls take
+    #  num_splits right after scale
+    _DECODE_ARGS = [c_p, c_int, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_p, c_int, c_int, c_int, c_int, c_int,
+                    c_int, c_int, c_int, c_f, c_p, c_sz, c_p]
+    # decode's arguments with (new_k, new_v, new_dtype) after q_dtype
+    _STEP_ARGS = [c_p, c_int, c_p, c_int, c_p, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_p, c_int, c_int, c_int,
+                  c_int, c_int, c_int, c_int, c_int, c_f, c_p, c_sz, c_p]
     sig = {
         "pkv_status_str": (ctypes.c_char_p, [c_int]),
         "pkv_abi_version": (c_int, []),
-        "pkv_decode_workspace_bytes": (c_sz, [c_int] * 7),
+        "pkv_decode_workspace_bytes": (c_sz, [c_int] * 5),
+        "pkv_decode_workspace_bytes_splits": (c_sz, [c_int] * 7),
         "pkv_decode_num_splits": (c_int, [c_int] * 7),
-        "pkv_paged_attention_decode": (c_int, [c_p, c_int, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_p,
-                                               c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_f, c_int,
-                                               c_p, c_sz, c_p]),
-        "pkv_decode_step": (c_int, [c_p, c_int, c_p, c_int, c_p, c_p, c_int, c_p, c_p, c_int, c_f, c_f, c_p, c_p,
-                                    c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_f, c_int, c_p, c_sz,
-                                    c_p]),
+        "pkv_paged_attention_decode": (c_int, _DECODE_ARGS),
+        "pkv_paged_attention_decode_splits": (c_int, _DECODE_ARGS[:20] + [c_int] + _DECODE_ARGS[20:]),
+        "pkv_decode_step": (c_int, _STEP_ARGS),
+        "pkv_decode_step_splits": (c_int, _STEP_ARGS[:23] + [c_int] + _STEP_ARGS[23:]),
         "pkv_multi_workspace_bytes": (c_sz, [c_int] * 8),
         "pkv_multi_num_splits": (c_int, [c_int] * 8),
         "pkv_paged_attention_multi": (c_int, [c_p, c_int, c_p, c_int, c_p, c_int, c_int, c_p, c_p, c_int, c_f, c_f,
@@ -126,8 +135,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def pkv_decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits=0):
-    return lib().pkv_decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)
+def pkv_decode_workspace_bytes(num_seqs, h_q, head_dim, max_context_len, block_size):
+    """Workspace bytes for any decode call with these sizes (any h_kv dividing
+    h_q, the library's split count)."""
+    return lib().pkv_decode_workspace_bytes(num_seqs, h_q, head_dim, max_context_len, block_size)
+
+
+def pkv_decode_workspace_bytes_splits(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits):
+    """Workspace bytes for a decode call with num_splits forced (0: the library's choice)."""
+    return lib().pkv_decode_workspace_bytes_splits(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len,
+                                                   num_splits)
 
 
 def pkv_decode_num_splits(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits=0):
@@ -135,19 +152,22 @@ def pkv_decode_num_splits(num_seqs, h_q, h_kv, head_dim, block_size, max_context
 
 
 def make_workspace(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits=0, device="cuda"):
-    """A zero-filled decode workspace (zero once; calls keep it reusable)."""
+    """A zero-filled decode workspace (zero once; calls keep it reusable),
+    sized by pkv_decode_workspace_bytes, or by pkv_decode_workspace_bytes_splits
+    for a forced split count."""
     import torch
-    n = pkv_decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)
+    if num_splits:
+        n = pkv_decode_workspace_bytes_splits(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)
+    else:
+        n = pkv_decode_workspace_bytes(num_seqs, h_q, head_dim, max_context_len, block_size)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
-                               scale=0.0, k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
-    """out[s, g, :] = attention of q[s, g, :] over sequence s's cached K/V.
-
-    q, out [S, Hq, D]; k_cache, v_cache [NB, Hkv, B, D] (uint8 = FP8 E4M3);
-    block_tables [S, MB] int32; context_lens [S] int32 (all on the GPU).
-    """
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace, scale, k_scale,
+                 v_scale, num_splits, stream):
+    """Checked, marshalled arguments of pkv_paged_attention_decode (num_splits
+    == 0) or pkv_paged_attention_decode_splits (num_splits inserted after
+    scale)."""
     import torch
     S, h_q, D = q.shape
     NB, h_kv, B, D2 = k_cache.shape
@@ -159,16 +179,30 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
         raise TypeError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_tables must be [S, MB] and context_lens [S]")
-    MB = block_tables.shape[1]
+    split_arg = (int(num_splits),) if num_splits else ()
+    return (_dev_ptr(out, "out"), dtype_code(out), _dev_ptr(q, "q"), dtype_code(q),
+            _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), dtype_code(k_cache),
+            float(k_scale), float(v_scale), _dev_ptr(block_tables, "block_tables"),
+            _dev_ptr(context_lens, "context_lens"), S, h_q, h_kv, D, B, NB, block_tables.shape[1],
+            int(max_context_len), float(scale), *split_arg, _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
+                               scale=0.0, k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+    """out[s, g, :] = attention of q[s, g, :] over sequence s's cached K/V.
+
+    q, out [S, Hq, D]; k_cache, v_cache [NB, Hkv, B, D] (uint8 = FP8 E4M3);
+    block_tables [S, MB] int32; context_lens [S] int32 (all on the GPU).
+    num_splits > 0 calls pkv_paged_attention_decode_splits with that count.
+    """
     if workspace is None:
-        workspace = make_workspace(S, h_q, h_kv, D, B, max_context_len, num_splits, device=q.device)
-    st = lib().pkv_paged_attention_decode(
-        _dev_ptr(out, "out"), dtype_code(out), _dev_ptr(q, "q"), dtype_code(q),
-        _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), dtype_code(k_cache),
-        float(k_scale), float(v_scale), _dev_ptr(block_tables, "block_tables"), _dev_ptr(context_lens, "context_lens"),
-        S, h_q, h_kv, D, B, NB, MB, int(max_context_len), float(scale), int(num_splits),
-        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(st, "pkv_paged_attention_decode")
+        workspace = make_workspace(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2], k_cache.shape[2],
+                                   max_context_len, num_splits, device=q.device)
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace, scale,
+                        k_scale, v_scale, num_splits, stream)
+    name = "pkv_paged_attention_decode_splits" if num_splits else "pkv_paged_attention_decode"
+    _check(getattr(lib(), name)(*args), name)
     return out
 
 
@@ -237,6 +271,8 @@ def pkv_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_le
 
 def _step_args(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace, scale,
                k_scale, v_scale, num_splits, stream):
+    """Checked, marshalled arguments of pkv_decode_step (num_splits == 0) or
+    pkv_decode_step_splits (num_splits inserted after scale)."""
     import torch
     S, h_q, D = q.shape
     NB, h_kv, B, D2 = k_cache.shape
@@ -250,11 +286,12 @@ def _step_args(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_len
         raise TypeError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    split_arg = (int(num_splits),) if num_splits else ()
     return (_dev_ptr(out, "out"), dtype_code(out), _dev_ptr(q, "q"), dtype_code(q), _dev_ptr(new_k, "new_k"),
             _dev_ptr(new_v, "new_v"), dtype_code(new_k), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
             dtype_code(k_cache), float(k_scale), float(v_scale), _dev_ptr(block_tables, "block_tables"),
             _dev_ptr(context_lens, "context_lens"), S, h_q, h_kv, D, B, NB, block_tables.shape[1],
-            int(max_context_len), float(scale), int(num_splits), _dev_ptr(workspace, "workspace"),
+            int(max_context_len), float(scale), *split_arg, _dev_ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream))
 
 
@@ -263,14 +300,16 @@ def pkv_decode_step(out, q, new_k, new_v, k_cache, v_cache, block_tables, contex
     """One decode step in one launch: new_k / new_v [S, Hkv, D] go to position
     context_lens[s] - 1 of each sequence (slot from its block table), then
     out[s, g, :] is the attention of q[s, g, :] over the context including
-    it.  Same bits as pkv_reshape_and_cache followed by the decode call."""
+    it.  Same bits as pkv_reshape_and_cache followed by the decode call.
+    num_splits > 0 calls pkv_decode_step_splits with that count."""
     if workspace is None:
         S, h_q, D = q.shape
         workspace = make_workspace(S, h_q, k_cache.shape[1], D, k_cache.shape[2], max_context_len, num_splits,
                                    device=q.device)
     args = _step_args(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace,
                       scale, k_scale, v_scale, num_splits, stream)
-    _check(lib().pkv_decode_step(*args), "pkv_decode_step")
+    name = "pkv_decode_step_splits" if num_splits else "pkv_decode_step"
+    _check(getattr(lib(), name)(*args), name)
     return out
 
 
@@ -292,18 +331,13 @@ class PreparedCall:
 
 def prepare_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
                                    workspace, scale=0.0, k_scale=1.0, v_scale=1.0, num_splits=0, stream=None):
-    """PreparedCall of pkv_paged_attention_decode (same arguments)."""
-    S, h_q, D = q.shape
-    NB, h_kv, B, _ = k_cache.shape
-    args = (_dev_ptr(out, "out"), dtype_code(out), _dev_ptr(q, "q"), dtype_code(q),
-            _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), dtype_code(k_cache),
-            float(k_scale), float(v_scale), _dev_ptr(block_tables, "block_tables"),
-            _dev_ptr(context_lens, "context_lens"), S, h_q, h_kv, D, B, NB, block_tables.shape[1],
-            int(max_context_len), float(scale), int(num_splits), _dev_ptr(workspace, "workspace"),
-            workspace.numel() * workspace.element_size(), _stream(stream))
-    call = PreparedCall(lib().pkv_paged_attention_decode, args, "pkv_paged_attention_decode",
+    """PreparedCall of pkv_paged_attention_decode (or its _splits variant for
+    num_splits > 0), same arguments."""
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace, scale,
+                        k_scale, v_scale, num_splits, stream)
+    name = "pkv_paged_attention_decode_splits" if num_splits else "pkv_paged_attention_decode"
+    return PreparedCall(getattr(lib(), name), args, name,
                         (out, q, k_cache, v_cache, block_tables, context_lens, workspace))
-    return call
 
 
 def prepare_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens, query_start, *,
@@ -318,10 +352,12 @@ def prepare_paged_attention_multi(out, q, k_cache, v_cache, block_tables, contex
 
 def prepare_decode_step(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
                         workspace, scale=0.0, k_scale=1.0, v_scale=1.0, num_splits=0, stream=None):
-    """PreparedCall of pkv_decode_step (same arguments)."""
+    """PreparedCall of pkv_decode_step (or pkv_decode_step_splits for
+    num_splits > 0), same arguments."""
     args = _step_args(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace,
                       scale, k_scale, v_scale, num_splits, stream)
-    return PreparedCall(lib().pkv_decode_step, args, "pkv_decode_step",
+    name = "pkv_decode_step_splits" if num_splits else "pkv_decode_step"
+    return PreparedCall(getattr(lib(), name), args, name,
                         (out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, workspace))
 
 

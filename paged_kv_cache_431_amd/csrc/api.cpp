@@ -87,10 +87,14 @@ int resolve_splits(int num_seqs, int h_kv, int max_context_len, int num_splits) 
   return std::max(1, n);
 }
 
+// Attention kernels are built for these head dims; another one is an
+// invalid argument, not a combination left out.
+bool attention_head_dim(int head_dim) { return head_dim == 64 || head_dim == 128; }
+
 bool decode_shape_ok(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_context_len,
                      int num_splits) {
-  return num_seqs >= 0 && h_q >= 1 && h_kv >= 1 && h_q % h_kv == 0 && head_dim >= 1 && block_size >= 1 &&
-         max_context_len >= 0 && num_splits >= 0;
+  return num_seqs >= 0 && h_q >= 1 && h_kv >= 1 && h_q % h_kv == 0 && attention_head_dim(head_dim) &&
+         block_size >= 1 && max_context_len >= 0 && num_splits >= 0;
 }
 
 // The address a kernel on the current device uses for p: p itself for memory
@@ -139,12 +143,13 @@ int resolve_multi_splits(int num_seqs, int h_q, int h_kv, int max_query_len, int
 
 // Decode (query_start == nullptr: one query token per sequence) and calls
 // with several query tokens per sequence share validation and launch.
-int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
-                  int num_query_tokens, int max_query_len, const void* new_k, const void* new_v, int new_dtype,
-                  const void* k_cache, const void* v_cache, int kv_dtype, float k_scale, float v_scale,
-                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
-                  int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
-                  float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
+                         int num_query_tokens, int max_query_len, const void* new_k, const void* new_v,
+                         int new_dtype, const void* k_cache, const void* v_cache, int kv_dtype, float k_scale,
+                         float v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                         int h_q, int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                         int max_context_len, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
   const bool multi = query_start != nullptr;
   const bool append = new_k != nullptr;
   if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return PKV_EINVAL;
@@ -157,7 +162,6 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   if (kv_dtype == PKV_FP8_E4M3 && !(k_scale > 0.f && std::isfinite(k_scale) && v_scale > 0.f && std::isfinite(v_scale)))
     return PKV_EINVAL;
 
-  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
   if (h_q / h_kv > pkv::kMaxGroup) return PKV_EUNSUPPORTED;
   if (out_dtype == PKV_FP8_E4M3 || q_dtype == PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
   const bool pair_ok = (q_dtype == kv_dtype) || (kv_dtype == PKV_FP8_E4M3 && q_dtype != PKV_F32);
@@ -239,15 +243,28 @@ int run_attention(void* out, int out_dtype, const void* q, int q_dtype, const in
   a.lpt_shift = matrix_core && balanced == 0 ? longest_first_shift(num_seqs, h_kv, max_context_len, num_splits, n,
                                                                    row_groups, waves_per_simd)
                                              : -1;
-  const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = pkv::launch_decode(a, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+// Workspace of a decode call with h_kv given and the split count forced
+// (num_splits > 0) or chosen by the library: enough for either assignment
+// (the balanced one is used on the matrix-core path only, which the shape
+// alone does not tell).
+size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_context_len,
+                              int num_splits) {
+  if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return 0;
+  const int n = resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
+  const int balanced = balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits);
+  return std::max(pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n).total,
+                  pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n, balanced).total);
 }
 
 }  // namespace
 
 extern "C" {
 
-const char* pkv_status_str(int status) {
+const char* pkv_status_str(pkv_status status) {
   switch (status) {
     case PKV_OK: return "PKV_OK";
     case PKV_EINVAL: return "PKV_EINVAL: invalid argument";
@@ -269,39 +286,82 @@ int pkv_decode_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int blo
   return resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
 }
 
-size_t pkv_decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
-                                  int max_context_len, int num_splits) {
-  if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return 0;
-  // enough for either assignment (the balanced one is used on the
-  // matrix-core path only, which the shape alone does not tell)
-  const int n = resolve_splits(num_seqs, h_kv, max_context_len, num_splits);
-  const int balanced = balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits);
-  return std::max(pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n).total,
-                  pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n, balanced).total);
+size_t pkv_decode_workspace_bytes(int num_seqs, int h_q, int head_dim, int max_context_len, int block_size) {
+  // the largest workspace over every KV-head count a call with these sizes
+  // may pass (the divisors of h_q), each with the library's split choice
+  size_t best = 0;
+  for (int h_kv = 1; h_kv <= h_q; ++h_kv) {
+    if (h_q % h_kv != 0) continue;
+    best = std::max(best, decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, 0));
+  }
+  return best;
 }
 
-int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
-                               const void* v_cache, int kv_dtype, float k_scale, float v_scale,
-                               const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q,
-                               int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
-                               int max_context_len, float scale, int num_splits, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+size_t pkv_decode_workspace_bytes_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                                         int max_context_len, int num_splits) {
+  return decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits);
+}
+
+pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                      const void* k_cache, const void* v_cache, pkv_dtype kv_dtype, float k_scale,
+                                      float v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                                      int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int num_blocks,
+                                      int max_blocks_per_seq, int max_context_len, float scale, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return run_attention(out, out_dtype, q, q_dtype, nullptr, 0, 1, nullptr, nullptr, 0, k_cache, v_cache, kv_dtype,
+                       k_scale, v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, 0, workspace, workspace_bytes,
+                       stream);
+}
+
+pkv_status pkv_paged_attention_decode_splits(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                             const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                             float k_scale, float v_scale, const int32_t* block_tables,
+                                             const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
+                                             int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                                             int max_context_len, float scale, int num_splits, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
   return run_attention(out, out_dtype, q, q_dtype, nullptr, 0, 1, nullptr, nullptr, 0, k_cache, v_cache, kv_dtype,
                        k_scale, v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size,
                        num_blocks, max_blocks_per_seq, max_context_len, scale, num_splits, workspace,
                        workspace_bytes, stream);
 }
 
-int pkv_decode_step(void* out, int out_dtype, const void* q, int q_dtype, const void* new_k, const void* new_v,
-                    int new_dtype, void* k_cache, void* v_cache, int kv_dtype, float k_scale, float v_scale,
-                    const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
-                    int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
-                    float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+pkv_status decode_step(void* out, int out_dtype, const void* q, int q_dtype, const void* new_k, const void* new_v,
+                       int new_dtype, void* k_cache, void* v_cache, int kv_dtype, float k_scale, float v_scale,
+                       const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
+                       int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+                       float scale, int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (num_seqs > 0 && (!new_k || !new_v)) return PKV_EINVAL;
   return run_attention(out, out_dtype, q, q_dtype, nullptr, 0, 1, num_seqs > 0 ? new_k : nullptr, new_v, new_dtype,
                        k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables, context_lens, num_seqs, h_q,
                        h_kv, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
                        num_splits, workspace, workspace_bytes, stream);
+}
+}  // namespace
+
+pkv_status pkv_decode_step(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* new_k,
+                           const void* new_v, pkv_dtype new_dtype, void* k_cache, void* v_cache, pkv_dtype kv_dtype,
+                           float k_scale, float v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                           int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_context_len, float scale, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return decode_step(out, out_dtype, q, q_dtype, new_k, new_v, new_dtype, k_cache, v_cache, kv_dtype, k_scale,
+                     v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, 0, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_step_splits(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                  const void* new_k, const void* new_v, pkv_dtype new_dtype, void* k_cache,
+                                  void* v_cache, pkv_dtype kv_dtype, float k_scale, float v_scale,
+                                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int h_q,
+                                  int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                                  int max_context_len, float scale, int num_splits, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return decode_step(out, out_dtype, q, q_dtype, new_k, new_v, new_dtype, k_cache, v_cache, kv_dtype, k_scale,
+                     v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 int pkv_multi_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
@@ -318,12 +378,13 @@ size_t pkv_multi_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, 
       .total;
 }
 
-int pkv_paged_attention_multi(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
-                              int num_query_tokens, int max_query_len, const void* k_cache, const void* v_cache,
-                              int kv_dtype, float k_scale, float v_scale, const int32_t* block_tables,
-                              const int32_t* context_lens, int num_seqs, int h_q, int h_kv, int head_dim,
-                              int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
-                              float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+pkv_status pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                     const int32_t* query_start, int num_query_tokens, int max_query_len,
+                                     const void* k_cache, const void* v_cache, pkv_dtype kv_dtype, float k_scale,
+                                     float v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                                     int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int num_blocks,
+                                     int max_blocks_per_seq, int max_context_len, float scale, int num_splits,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!multi_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len, num_splits))
     return PKV_EINVAL;
   if (num_query_tokens < 0) return PKV_EINVAL;
@@ -334,9 +395,10 @@ int pkv_paged_attention_multi(void* out, int out_dtype, const void* q, int q_dty
                        workspace, workspace_bytes, stream);
 }
 
-int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype, void* k_cache, void* v_cache,
-                          int kv_dtype, float k_scale, float v_scale, const int64_t* slot_mapping, int num_tokens,
-                          int h_kv, int head_dim, int block_size, int num_blocks, void* stream) {
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype in_dtype, void* k_cache,
+                                 void* v_cache, pkv_dtype kv_dtype, float k_scale, float v_scale,
+                                 const int64_t* slot_mapping, int num_tokens, int h_kv, int head_dim, int block_size,
+                                 int num_blocks, hipStream_t stream) {
   if (num_tokens < 0 || h_kv < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1) return PKV_EINVAL;
   if (!valid_dtype(in_dtype) || !valid_dtype(kv_dtype)) return PKV_EINVAL;
   if (num_tokens == 0) return PKV_OK;
@@ -348,13 +410,12 @@ int pkv_reshape_and_cache(const void* key, const void* value, int in_dtype, void
   if (in_dtype != kv_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
   const hipError_t e =
       pkv::launch_reshape_and_cache(key, value, in_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, slot_mapping,
-                                    num_tokens, h_kv, head_dim, block_size, num_blocks,
-                                    static_cast<hipStream_t>(stream));
+                                    num_tokens, h_kv, head_dim, block_size, num_blocks, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, const int32_t* block_pairs, int num_pairs, int h_kv,
-                    int head_dim, int block_size, int num_blocks, void* stream) {
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype kv_dtype, const int32_t* block_pairs,
+                           int num_pairs, int h_kv, int head_dim, int block_size, int num_blocks, hipStream_t stream) {
   if (num_pairs < 0 || h_kv < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1) return PKV_EINVAL;
   if (!valid_dtype(kv_dtype)) return PKV_EINVAL;
   if (num_pairs == 0) return PKV_OK;
@@ -363,13 +424,13 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, const int32_t* b
   const int64_t block_bytes = (int64_t)h_kv * block_size * head_dim * kElementBytes[kv_dtype];
   if (block_bytes % 16 != 0) return PKV_EUNSUPPORTED;
   const hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, block_pairs, num_pairs, block_bytes,
-                                               num_blocks, num_blocks, static_cast<hipStream_t>(stream));
+                                               num_blocks, num_blocks, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-int pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* src_k, const void* src_v,
-                    int src_num_blocks, int kv_dtype, const int32_t* block_pairs, int num_pairs, int h_kv,
-                    int head_dim, int block_size, void* stream) {
+pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* src_k, const void* src_v,
+                           int src_num_blocks, pkv_dtype kv_dtype, const int32_t* block_pairs, int num_pairs, int h_kv,
+                           int head_dim, int block_size, hipStream_t stream) {
   if (num_pairs < 0 || h_kv < 1 || head_dim < 1 || block_size < 1 || dst_num_blocks < 1 || src_num_blocks < 1)
     return PKV_EINVAL;
   if (!valid_dtype(kv_dtype)) return PKV_EINVAL;
@@ -385,7 +446,7 @@ int pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* sr
       !device_address(src_v, &sv) || !device_address(block_pairs, &pp))
     return PKV_EINVAL;
   const hipError_t e = pkv::launch_copy_blocks(dk, dv, sk, sv, static_cast<const int32_t*>(pp), num_pairs, block_bytes,
-                                               src_num_blocks, dst_num_blocks, static_cast<hipStream_t>(stream));
+                                               src_num_blocks, dst_num_blocks, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

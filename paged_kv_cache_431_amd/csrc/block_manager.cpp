@@ -42,7 +42,7 @@ int64_t blocks_for(int64_t tokens, int32_t block_size) { return (tokens + block_
 
 extern "C" {
 
-int pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pkv_bm** out) {
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pkv_bm** out) {
   if (out == nullptr || num_blocks <= 0 || block_size <= 0) return PKV_EINVAL;
   *out = nullptr;
   pkv_bm* bm = new (std::nothrow) pkv_bm();
@@ -70,8 +70,8 @@ int pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_or
 
 void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
 
-int pkv_bm_append(pkv_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out, int32_t* cow_src,
-                  int32_t* cow_dst) {
+pkv_status pkv_bm_append(pkv_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out, int32_t* cow_src,
+                         int32_t* cow_dst) {
   if (bm == nullptr || seq < 0 || n_tokens < 0) return PKV_EINVAL;
   if (cow_src) *cow_src = -1;
   if (cow_dst) *cow_dst = -1;
@@ -109,7 +109,7 @@ int pkv_bm_append(pkv_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out,
   return PKV_OK;
 }
 
-int pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child) {
+pkv_status pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child) {
   if (bm == nullptr || child < 0) return PKV_EINVAL;
   auto p = bm->seqs.find(parent);
   if (p == bm->seqs.end() || bm->seqs.count(child)) return PKV_EINVAL;
@@ -119,7 +119,7 @@ int pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child) {
   return PKV_OK;
 }
 
-int pkv_bm_free(pkv_bm* bm, int32_t seq) {
+pkv_status pkv_bm_free(pkv_bm* bm, int32_t seq) {
   if (bm == nullptr) return PKV_EINVAL;
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PKV_EINVAL;
@@ -130,7 +130,7 @@ int pkv_bm_free(pkv_bm* bm, int32_t seq) {
   return PKV_OK;
 }
 
-int pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t cap, int32_t* n_blocks,
+pkv_status pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t cap, int32_t* n_blocks,
                        int32_t* n_tokens) {
   if (bm == nullptr) return PKV_EINVAL;
   auto it = bm->seqs.find(seq);
@@ -145,7 +145,7 @@ int pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t cap,
   return PKV_OK;
 }
 
-int pkv_bm_export(const pkv_bm* bm, const int32_t* seqs, int32_t num_seqs, int32_t* tables, int32_t max_blocks,
+pkv_status pkv_bm_export(const pkv_bm* bm, const int32_t* seqs, int32_t num_seqs, int32_t* tables, int32_t max_blocks,
                   int32_t* context_lens) {
   if (bm == nullptr || num_seqs < 0 || max_blocks < 0 || (num_seqs > 0 && (seqs == nullptr || tables == nullptr)))
     return PKV_EINVAL;
@@ -170,7 +170,7 @@ int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block) {
   return bm->refcount[block];
 }
 
-int pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
+pkv_status pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
   if (bm == nullptr) return PKV_EINVAL;
   if (n) *n = (int32_t)bm->free_list.size();
   if (out != nullptr) {

@@ -139,6 +139,10 @@ struct Params {
 
 struct Item {
   int s, kvh, unit, split, ctx, n_tiles, n_splits_seq, t_begin, t_end;
+  // decode step: the sequence's context length, before clamping, lies in
+  // [1, table capacity], so position ctx - 1 is the new token's own slot (a
+  // longer one is attended over the table's tokens and writes nothing)
+  bool append;
   int rt, m, q0;  // several query tokens: first row tile, query tokens of the sequence, first query row
   // balanced ranges (bal_r > 0): range length, first workgroup holding a
   // piece of this pair, first tile of the pair in the flattened order
@@ -185,8 +189,8 @@ __device__ int block_exclusive_scan(int x, int* part) {
 // fill the end (the longest-processing-time-first rule of list scheduling):
 // the launch no longer waits on a long pair that started late.  Rank r of
 // the sequences ordered by tile count (>> p.lpt_shift), longest first, ties
-// in index order; *ctx_out receives its context length, clamped as items
-// clamp it.  Every thread of the workgroup calls this (at most kLptMaxSeqs
+// in index order; *ctx_out receives its context length as stored (items
+// clamp it).  Every thread of the workgroup calls this (at most kLptMaxSeqs
 // sequences); lds holds kLptBins + 8 ints.
 __device__ int lpt_sequence(const Params& p, int r, int* lds, int* ctx_out) {
   constexpr int PER = kLptMaxSeqs / kDecodeThreads;  // consecutive sequences per thread
@@ -200,9 +204,9 @@ __device__ int lpt_sequence(const Params& p, int r, int* lds, int* ctx_out) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int s = t * PER + i;
-    int c = s < S ? p.context_lens[s] : 0;
-    c = c < 0 ? 0 : (c > cap ? cap : c);
-    ctx[i] = c;
+    const int raw = s < S ? p.context_lens[s] : 0;
+    const int c = raw < 0 ? 0 : (raw > cap ? cap : raw);
+    ctx[i] = raw;
     bin[i] = s < S ? min(((c + kTileTokens - 1) / kTileTokens) >> p.lpt_shift, kLptBins - 1) : -1;
   }
   for (int b = t; b < kLptBins; b += kDecodeThreads) hist[b] = 0;
@@ -278,8 +282,9 @@ __device__ __forceinline__ bool get_item(const Params& p, Item& it, int* lds) {
   } else {
     it.s = base / p.h_kv;
     ctx = p.context_lens[it.s];
-    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   }
+  it.append = ctx >= 1 && ctx <= cap;
+  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   it.kvh = base - it.s * p.h_kv;
   it.ctx = ctx;
   int n_tok = ctx;  // positions any row of the item attends to: [0, n_tok)
@@ -593,6 +598,7 @@ __device__ bool balanced_next(const Params& p, const int* pre, Balanced& b, Item
   it.kvh = kvh;
   it.unit = lo * H + kvh;
   const int ctx = p.context_lens[lo];
+  it.append = ctx >= 1 && ctx <= b.cap;
   it.ctx = ctx < 0 ? 0 : (ctx > b.cap ? b.cap : ctx);
   it.n_tiles = ts;
   it.t_begin = b.pos - first;
@@ -886,7 +892,8 @@ decode_mfma_kernel(Params p) {
     // that tile with the new rows (staged in LDS at the start) in place of the
     // loaded ones, and writes them to the pool after its last tile.  No other
     // wave or workgroup reads that position, so nothing waits for the write.
-    const bool owner = AP && it.t_end == it.n_tiles && wb <= it.n_tiles - 1 && it.n_tiles - 1 < wb + n_my;
+    const bool owner =
+        AP && it.append && it.t_end == it.n_tiles && wb <= it.n_tiles - 1 && it.n_tiles - 1 < wb + n_my;
     const int last_tok0 = (it.n_tiles - 1) * kTileTokens;
     int last_phys = -1;  // physical block of the last position (owner wave)
 
@@ -1388,37 +1395,6 @@ hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_
 }
 
 }  // namespace
-
-WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits,
-                                        int balanced_workgroups) {
-  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const size_t units = (size_t)num_seqs * h_kv;
-  const size_t rows = balanced_workgroups > 0
-                          ? (size_t)balanced_workgroups * 2 * (h_q / h_kv)  // two slots per workgroup, G rows each
-                          : (size_t)num_seqs * h_q * num_splits;           // units * G * splits
-  WorkspaceLayout L;
-  L.counters = 0;
-  L.ml = align(units * sizeof(int32_t));
-  L.acc = L.ml + align(rows * 2 * sizeof(float));
-  L.total = L.acc + align(rows * head_dim * sizeof(float));
-  return L;
-}
-
-WorkspaceLayout multi_workspace_layout(int num_seqs, int h_kv, int head_dim, int row_tiles, int num_splits) {
-  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
-  // one counter and 16 partial rows per split for every row tile the
-  // workgroups hold (row groups x tiles per workgroup: one more than
-  // row_tiles when an odd count is held two by two)
-  const size_t units = (((size_t)num_seqs * h_kv + 7) / 8) * 8 * multi_row_groups(row_tiles) *
-                       multi_tiles_per_workgroup(row_tiles);
-  const size_t rows = units * num_splits * 16;
-  WorkspaceLayout L;
-  L.counters = 0;
-  L.ml = align(units * sizeof(int32_t));
-  L.acc = L.ml + align(rows * 2 * sizeof(float));
-  L.total = L.acc + align(rows * head_dim * sizeof(float));
-  return L;
-}
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const bool multi = a.query_start != nullptr;

@@ -23,6 +23,9 @@ TOL = {  # max |err| and rel-L2 against the float64 oracle
     "f32": (2e-2, 1e-3),
 }
 
+# expected decode rows of a workload (oracle output), computed once per session
+_ORACLE_DECODE = {}
+
 _BITS = {torch.float32: (torch.int32, np.uint32), torch.float16: (torch.int16, np.uint16),
          torch.bfloat16: (torch.int16, np.uint16), torch.uint8: (torch.uint8, np.uint8)}
 
@@ -101,6 +104,15 @@ class Case:
             to_bits(self.t.q), kc, vc, self.rp.block_tables, self.plan.context_lens, q_dtype=wl.q_dtype,
             kv_dtype=wl.kv_dtype, block_size=wl.block_size, scale=1.0 / math.sqrt(wl.head_dim),
             k_scale=self.t.k_scale, v_scale=self.t.v_scale, seqs=seqs)
+
+    def oracle_decode_all(self):
+        """The oracle's output for every row of the decode step, kept per
+        workload for the session: a Case is a pure function of its seeded
+        workload, so every Case of one workload has the same expected rows."""
+        key = self.wl
+        if key not in _ORACLE_DECODE:
+            _ORACLE_DECODE[key] = self.oracle_decode()
+        return _ORACLE_DECODE[key]
 
     def oracle_multi(self, q, query_start, seqs=None):
         wl = self.wl

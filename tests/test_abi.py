@@ -32,9 +32,87 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
 
 
+# The boundary's core calls, parameter by parameter (type, name), in the
+# order the statement of the problem gives them: the header must declare
+# exactly these, so that a caller written against that statement can neither
+# mis-order same-typed integers nor pass a parameter the call does not take.
+BOUNDARY = {
+    "pkv_status_str": ("const char*", [("pkv_status", "status")]),
+    "pkv_decode_workspace_bytes": ("size_t", [("int", "num_seqs"), ("int", "h_q"), ("int", "head_dim"),
+                                              ("int", "max_context_len"), ("int", "block_size")]),
+    "pkv_paged_attention_decode": ("pkv_status", [
+        ("void*", "out"), ("pkv_dtype", "out_dtype"), ("const void*", "q"), ("pkv_dtype", "q_dtype"),
+        ("const void*", "k_cache"), ("const void*", "v_cache"), ("pkv_dtype", "kv_dtype"), ("float", "k_scale"),
+        ("float", "v_scale"), ("const int32_t*", "block_tables"), ("const int32_t*", "context_lens"),
+        ("int", "num_seqs"), ("int", "h_q"), ("int", "h_kv"), ("int", "head_dim"), ("int", "block_size"),
+        ("int", "num_blocks"), ("int", "max_blocks_per_seq"), ("int", "max_context_len"), ("float", "scale"),
+        ("void*", "workspace"), ("size_t", "workspace_bytes"), ("hipStream_t", "stream")]),
+    "pkv_reshape_and_cache": ("pkv_status", [
+        ("const void*", "key"), ("const void*", "value"), ("pkv_dtype", "in_dtype"), ("void*", "k_cache"),
+        ("void*", "v_cache"), ("pkv_dtype", "kv_dtype"), ("float", "k_scale"), ("float", "v_scale"),
+        ("const int64_t*", "slot_mapping"), ("int", "num_tokens"), ("int", "h_kv"), ("int", "head_dim"),
+        ("int", "block_size"), ("int", "num_blocks"), ("hipStream_t", "stream")]),
+    "pkv_bm_create": ("pkv_status", [("int32_t", "num_blocks"), ("int32_t", "block_size"),
+                                     ("const int32_t*", "free_order"), ("pkv_bm**", "out")]),
+    "pkv_bm_destroy": ("void", [("pkv_bm*", "bm")]),
+    "pkv_bm_append": ("pkv_status", [("pkv_bm*", "bm"), ("int32_t", "seq"), ("int32_t", "n_tokens"),
+                                     ("int64_t*", "slots_out"), ("int32_t*", "cow_src"), ("int32_t*", "cow_dst")]),
+    "pkv_bm_fork": ("pkv_status", [("pkv_bm*", "bm"), ("int32_t", "parent"), ("int32_t", "child")]),
+    "pkv_bm_free": ("pkv_status", [("pkv_bm*", "bm"), ("int32_t", "seq")]),
+    "pkv_bm_block_table": ("pkv_status", [("const pkv_bm*", "bm"), ("int32_t", "seq"), ("int32_t*", "out"),
+                                          ("int32_t", "cap"), ("int32_t*", "n_blocks"), ("int32_t*", "n_tokens")]),
+    "pkv_bm_num_free": ("int32_t", [("const pkv_bm*", "bm")]),
+    "pkv_bm_refcount": ("int32_t", [("const pkv_bm*", "bm"), ("int32_t", "block")]),
+}
+
+
+def declarations():
+    """name -> (return type, [(parameter type, parameter name)]) for every
+    function the header declares, white space normalised."""
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"#.*", "", text)
+    out = {}
+    for m in re.finditer(r"([A-Za-z_][\w\s\*]*?)\b(pkv_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", text):
+        ret = re.sub(r"\s+", " ", m.group(1)).strip().split(";")[-1].strip()
+        ret = re.sub(r"\s*\*", "*", ret.split("}")[-1].strip())
+        params = []
+        body = m.group(3).strip()
+        if body and body != "void":
+            for p in body.split(","):
+                p = re.sub(r"\s+", " ", p).strip()
+                name = re.findall(r"(\w+)$", p)[0]
+                typ = re.sub(r"\s*\*", "*", p[: -len(name)].strip())
+                params.append((typ, name))
+        out[m.group(2)] = (ret, params)
+    return out
+
+
+def test_header_matches_the_boundary_parameter_by_parameter():
+    decl = declarations()
+    for name, (ret, params) in BOUNDARY.items():
+        assert name in decl, f"{name} is not declared"
+        assert decl[name][0] == ret, f"{name}: returns {decl[name][0]}, expected {ret}"
+        assert decl[name][1] == params, f"{name}: parameters {decl[name][1]}\nexpected {params}"
+
+
+def test_split_forcing_calls_are_decode_plus_one_named_parameter():
+    """The tuning variants take decode's (and the step's) parameters with
+    num_splits after scale, under names of their own."""
+    decl = declarations()
+    base = decl["pkv_paged_attention_decode"][1]
+    i = [n for _, n in base].index("scale") + 1
+    assert decl["pkv_paged_attention_decode_splits"][1] == base[:i] + [("int", "num_splits")] + base[i:]
+    step = decl["pkv_decode_step"][1]
+    j = [n for _, n in step].index("scale") + 1
+    assert decl["pkv_decode_step_splits"][1] == step[:j] + [("int", "num_splits")] + step[j:]
+    assert [n for _, n in decl["pkv_decode_workspace_bytes_splits"][1]] == [
+        "num_seqs", "h_q", "h_kv", "head_dim", "block_size", "max_context_len", "num_splits"]
+
+
 def test_abi_version_and_status_strings():
     L = pkv.lib()
-    assert L.pkv_abi_version() == 1
+    assert L.pkv_abi_version() == 2
     for code in range(6):
         assert L.pkv_status_str(code).startswith(b"PKV_")
     assert b"unknown" in L.pkv_status_str(99)
@@ -44,32 +122,44 @@ def test_workspace_and_split_sizing():
     # 47 sequences x 825 tokens, 64 query heads on 8 KV heads, d = 128
     n = pkv.pkv_decode_num_splits(47, 64, 8, 128, 16, 825)
     assert n >= 1
-    ws = pkv.pkv_decode_workspace_bytes(47, 64, 8, 128, 16, 825)
+    ws = pkv.pkv_decode_workspace_bytes_splits(47, 64, 8, 128, 16, 825, 0)
     rows = 47 * 64 * n
     assert ws >= rows * 128 * 4 + rows * 8 + 47 * 8 * 4
-    assert pkv.pkv_decode_workspace_bytes(47, 64, 8, 128, 16, 825, 5) >= 47 * 64 * 5 * 128 * 4
+    assert pkv.pkv_decode_workspace_bytes_splits(47, 64, 8, 128, 16, 825, 5) >= 47 * 64 * 5 * 128 * 4
+    # the boundary's sizing (no h_kv) covers every KV-head count dividing h_q
+    full = pkv.pkv_decode_workspace_bytes(47, 64, 128, 825, 16)
+    for h_kv in (1, 2, 4, 8, 16, 32, 64):
+        assert full >= pkv.pkv_decode_workspace_bytes_splits(47, 64, h_kv, 128, 16, 825, 0)
+    assert full == max(pkv.pkv_decode_workspace_bytes_splits(47, 64, h, 128, 16, 825, 0)
+                       for h in (1, 2, 4, 8, 16, 32, 64))
     # 10 sequences of up to 12,000 tokens on 2 KV heads: balanced ranges over
     # ceil(20 x 750 / 64) = 235 workgroups, two partial slots of 8 rows each
-    assert pkv.pkv_decode_workspace_bytes(10, 16, 2, 128, 16, 12000) >= 235 * 2 * 8 * (128 + 2) * 4
+    assert pkv.pkv_decode_workspace_bytes_splits(10, 16, 2, 128, 16, 12000, 0) >= 235 * 2 * 8 * (128 + 2) * 4
+    assert pkv.pkv_decode_workspace_bytes(10, 16, 128, 12000, 16) >= 235 * 2 * 8 * (128 + 2) * 4
     assert pkv.pkv_decode_num_splits(10, 16, 2, 128, 16, 12000) == 12       # 235 workgroups over 20 pairs
     assert pkv.pkv_decode_num_splits(10, 16, 2, 128, 16, 12000, 3) == 3     # forced: one per pair and split
     assert pkv.pkv_decode_num_splits(47, 64, 8, 128, 16, 825, 5) == 5
     assert pkv.pkv_decode_num_splits(4, 8, 2, 64, 16, 0) == 1
     # invalid shapes size to 0
-    assert pkv.pkv_decode_workspace_bytes(4, 6, 4, 64, 16, 100) == 0
+    assert pkv.pkv_decode_workspace_bytes_splits(4, 6, 4, 64, 16, 100, 0) == 0
+    assert pkv.pkv_decode_workspace_bytes(4, 8, 96, 100, 16) == 0       # head_dim 96 is invalid
+    assert pkv.pkv_decode_workspace_bytes(-1, 8, 64, 100, 16) == 0
     assert pkv.pkv_decode_num_splits(-1, 8, 2, 64, 16, 100) == 0
 
 
 def _decode(**over):
     args = dict(out=1, out_dtype=0, q=1, q_dtype=2, k=1, v=1, kv=2, ks=1.0, vs=1.0, bt=1, cl=1, S=4, hq=8, hkv=2,
-                d=128, bs=16, nb=10, mb=4, maxctx=64, scale=0.0, splits=0, ws=1, wsb=1 << 30, stream=None)
+                d=128, bs=16, nb=10, mb=4, maxctx=64, scale=0.0, splits=None, ws=1, wsb=1 << 30, stream=None)
     args.update(over)
     a = args
     P = ctypes.c_void_p
-    return pkv.lib().pkv_paged_attention_decode(
-        P(a["out"]), a["out_dtype"], P(a["q"]), a["q_dtype"], P(a["k"]), P(a["v"]), a["kv"], a["ks"], a["vs"],
-        P(a["bt"]), P(a["cl"]), a["S"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["maxctx"],
-        a["scale"], a["splits"], P(a["ws"]), a["wsb"], a["stream"])
+    head = (P(a["out"]), a["out_dtype"], P(a["q"]), a["q_dtype"], P(a["k"]), P(a["v"]), a["kv"], a["ks"], a["vs"],
+            P(a["bt"]), P(a["cl"]), a["S"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["maxctx"],
+            a["scale"])
+    tail = (P(a["ws"]), a["wsb"], a["stream"])
+    if a["splits"] is None:
+        return pkv.lib().pkv_paged_attention_decode(*head, *tail)
+    return pkv.lib().pkv_paged_attention_decode_splits(*head, a["splits"], *tail)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -82,7 +172,9 @@ def _decode(**over):
     (dict(kv=7), pkv.PKV_EINVAL),
     (dict(kv=3, ks=0.0), pkv.PKV_EINVAL),           # FP8 needs positive scales
     (dict(scale=float("nan")), pkv.PKV_EINVAL),
-    (dict(d=96), pkv.PKV_EUNSUPPORTED),
+    (dict(d=96), pkv.PKV_EINVAL),                   # the kernels are built for head_dim 64 and 128
+    (dict(d=96, splits=2), pkv.PKV_EINVAL),
+    (dict(splits=-1), pkv.PKV_EINVAL),
     (dict(hq=34, hkv=2), pkv.PKV_EUNSUPPORTED),     # group of 17
     (dict(q_dtype=0), pkv.PKV_EUNSUPPORTED),        # fp32 query on a bf16 cache
     (dict(out_dtype=3), pkv.PKV_EUNSUPPORTED),
@@ -116,7 +208,7 @@ def _multi(**over):
     (dict(kv=0, q_dtype=0), pkv.PKV_EUNSUPPORTED),  # fp32 caches: vector path, one query token only
     (dict(bs=8, mb=8), pkv.PKV_EUNSUPPORTED),       # blocks that are not whole 16-token tiles
     (dict(bs=48, mb=2), pkv.PKV_EUNSUPPORTED),      # three tiles per block
-    (dict(d=96), pkv.PKV_EUNSUPPORTED),
+    (dict(d=96), pkv.PKV_EINVAL),
     (dict(wsb=16), pkv.PKV_EWORKSPACE),
     (dict(T=0), pkv.PKV_OK),                        # no query rows: nothing launched
     (dict(S=0, qs=None), pkv.PKV_OK),
@@ -192,7 +284,7 @@ def test_decode_step_rejects_bad_arguments_without_launching():
     P = ctypes.c_void_p
     call = lambda **o: L.pkv_decode_step(P(1), 0, P(1), 2, P(o.get("nk", 1)), P(1), o.get("nd", 2), P(1), P(1),
                                          o.get("kv", 2), 1.0, 1.0, P(1), P(1), o.get("S", 4), 8, 2, 128,
-                                         o.get("bs", 16), 10, 4, 64, 0.0, 0, P(1), o.get("wsb", 16), None)
+                                         o.get("bs", 16), 10, 4, 64, 0.0, P(1), o.get("wsb", 16), None)
     assert call(nk=None) == pkv.PKV_EINVAL
     assert call(nd=7) == pkv.PKV_EINVAL
     assert call(nd=1) == pkv.PKV_EUNSUPPORTED                # f16 tokens into a bf16 pool

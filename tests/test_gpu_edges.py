@@ -124,3 +124,35 @@ def test_bad_device_data_stays_inside_its_sequence(kv):
         valid_blocks = valid_blocks[(valid_blocks >= 0) & (valid_blocks < nb)]
         assert np.array_equal(kb[valid_blocks], k0[valid_blocks])
         assert np.array_equal(vb[valid_blocks], v0[valid_blocks])
+
+
+@pytest.mark.parametrize("types", [("bf16", "bf16", "bf16"), ("bf16", "fp8", "bf16")], ids=lambda t: "-".join(t))
+def test_step_writes_nothing_past_a_full_table(types):
+    """A context length beyond the table's capacity is attended over the
+    table's tokens, and the step writes no new token for it: position
+    capacity - 1 holds a cached token of its own.  Sequence 0 fills its table
+    exactly (5 blocks of 16); its length is raised past the table, and its
+    blocks must keep every byte while the others take their new tokens as
+    usual and keep their output bits."""
+    q, kv, new = types
+    c = Case(workloads.Workload(f"edges-full-{kv}", 4, 16, 2, 128, 16, q, kv, new, 74,
+                                contexts=(80, 17, 33, 5), extra_blocks=4))
+    wl = c.wl
+    mb = c.block_tables.shape[1]
+    assert mb * wl.block_size == 80 and (c.rp.block_tables[0] >= 0).all(), "sequence 0 fills its table"
+    c.scatter()
+    clean = c.decode()
+    lens = c.context_lens.clone()
+    lens[0] = 80 + 7
+    print(f"[case] {wl.name} lengths {lens.tolist()} (capacity 80)", flush=True)
+    k0, v0 = to_bits(c.t.k_cache).copy(), to_bits(c.t.v_cache).copy()
+    out = torch.empty_like(clean)
+    pkv.pkv_decode_step(out, c.t.q, c.t.new_k, c.t.new_v, c.t.k_cache, c.t.v_cache, c.block_tables, lens,
+                        max_context_len=c.plan.max_context_len, k_scale=c.t.k_scale, v_scale=c.t.v_scale)
+    torch.cuda.synchronize()
+    # the other sequences rewrote their new tokens where the scatter had put
+    # them, and sequence 0 wrote nothing: the pools are byte for byte as before
+    assert np.array_equal(to_bits(c.t.k_cache), k0), "K pool changed"
+    assert np.array_equal(to_bits(c.t.v_cache), v0), "V pool changed"
+    # sequence 0 attends over its 80 cached tokens: decode's bits
+    assert torch.equal(out, clean), "outputs differ from decode over the table's tokens"

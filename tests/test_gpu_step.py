@@ -4,7 +4,6 @@ the scatter followed by decode on identical seeded inputs, and the oracle's
 result within the decode tolerances.  The new tokens' slots start poisoned
 (NaN), so a step that attended over the stale slot could not match."""
 
-import numpy as np
 import pytest
 import torch
 
@@ -34,21 +33,25 @@ def step(c, num_splits=0, out_dtype=torch.float32):
     return out
 
 
-def check_step(wl, num_splits=0, oracle_seqs=None, label=None):
+def check_step(wl, num_splits=0, label=None, all_rows_cached=False):
+    """The step against scatter + decode (bits of the output and of both
+    pools) and against the oracle on every output row."""
     label = label or wl.name
     print(f"[case] {label} splits={num_splits}", flush=True)
     two = Case(wl)
     two.scatter()
     ref_out = two.decode(num_splits=num_splits)
+    torch.cuda.synchronize()
+    two_k, two_v = two.t.k_cache.view(torch.uint8), two.t.v_cache.view(torch.uint8)
     one = Case(wl)
     out = step(one, num_splits)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out), f"{label}: step output differs from scatter + decode"
-    assert torch.equal(one.t.k_cache.view(torch.uint8), two.t.k_cache.view(torch.uint8)), f"{label}: K pool"
-    assert torch.equal(one.t.v_cache.view(torch.uint8), two.t.v_cache.view(torch.uint8)), f"{label}: V pool"
-    ref = one.oracle_decode(seqs=oracle_seqs)
-    rows = oracle_seqs
-    assert_close(out, ref, wl.kv_dtype, seqs=rows, label=label)
+    assert torch.equal(one.t.k_cache.view(torch.uint8), two_k), f"{label}: K pool"
+    assert torch.equal(one.t.v_cache.view(torch.uint8), two_v), f"{label}: V pool"
+    del two_k, two_v
+    ref = one.oracle_decode_all() if all_rows_cached else one.oracle_decode()
+    assert_close(out, ref, wl.kv_dtype, label=f"{label} all rows")
 
 
 @pytest.mark.parametrize("types", MFMA_TYPES, ids=lambda t: "-".join(t))
@@ -68,15 +71,25 @@ def test_step_with_forced_splits(splits, types):
     check_step(wl, num_splits=splits, label=f"{wl.name}-splits{splits}")
 
 
-@pytest.mark.parametrize("name", ["gqa70b-bf16-47x825", "fp8-prefix-32xU32768"])
+@pytest.mark.parametrize("name", sorted(workloads.NAMED))
 def test_step_on_named_workload(name):
+    """The one-launch step the bench times, on every named workload at full
+    size (the fp32 one has no one-launch step)."""
     wl = workloads.get(name)
-    rng = np.random.default_rng(55)
-    seqs = sorted(set(rng.choice(wl.num_seqs, 4, replace=False).tolist()))
-    check_step(wl, oracle_seqs=seqs, label=name)
+    if wl.kv_dtype == "f32":
+        pytest.skip("fp32 caches take the vector path, which has no one-launch step")
+    check_step(wl, label=name, all_rows_cached=True)
 
 
 def test_fp32_cache_is_unsupported():
     c = Case(small(8, 2, 64, 16, "f32", "f32", "f32", contexts=(20, 5)))
     with pytest.raises(pkv.PkvError, match="PKV_EUNSUPPORTED"):
         step(c)
+
+
+def test_step_on_gqa70b_with_32_token_blocks():
+    """The one-launch step of the headline shape with 32-token blocks: bits of
+    scatter + decode, every row against the oracle."""
+    wl = workloads.get("gqa70b-bf16-47x825")
+    wl = workloads.replace(wl, name=f"{wl.name}-b32", block_size=32, num_blocks=wl.num_blocks * wl.block_size // 32)
+    check_step(wl, label=wl.name)
