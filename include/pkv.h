@@ -337,13 +337,13 @@ pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const v
  * Host block manager (no device memory; pure host bookkeeping)
  *
  * Blocks are handed out only as a sequence grows ("AI Engineering
- * Visualised: KV cache", intro), one free block at a time with no relocation
- * of earlier blocks ("Paged KV Cache" tutorial, "Answer Key", question 2); a
- * block returns to the free list once nothing references it, and sequences
- * share prefix blocks by reference count with copy-on-write when they
- * diverge inside a shared tail block (same tutorial, "Block Tables and
- * Sharing"; "KV cache and PagedAttention in serving", "The bonus: sharing
- * via copy-on-write").
+ * Visualised: KV cache", intro), one by one, and a sequence's earlier blocks
+ * never move ("Paged KV Cache" tutorial, "Answer Key", question 2); a block
+ * returns to the free list once nothing references it, and sequences share
+ * prefix blocks by reference count, a sequence that appends into a shared,
+ * partly filled last block first moving to a block of its own (same
+ * tutorial, "Block Tables and Sharing"; "KV cache and PagedAttention in
+ * serving", "The bonus: sharing via copy-on-write").
  *
  * Policy: the free list is FIFO (take from the front, released blocks go to
  * the back, a freed sequence releases in block-table order), seeded by

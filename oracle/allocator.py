@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 What the pages fix
   * Blocks are handed out only as a sequence actually grows ([UD] intro;
     [AF] "PagedAttention": new blocks are allocated on demand).
-  * Growing a sequence claims one free physical block at a time and never
-    relocates earlier blocks ([OT] "Answer Key", question 2).
+  * A sequence that grows takes free blocks one by one, as it needs them;
+    the blocks it already holds stay where they are ([OT] "Answer Key",
+    question 2).
   * A physical block goes back to the free list once no sequence references
     it ([OT] "Block Tables and Sharing").
   * Reference counting lets sequences point at the same prefix blocks; a

@@ -6,9 +6,10 @@ What the pages fix
   * Each sequence's KV cache is cut into fixed-size blocks stored anywhere in
     the pool; a per-sequence block table maps logical block j to a physical
     block ([UD] intro; [AF] "PagedAttention: virtual memory for GPUs").
-  * The model still sees one continuous token sequence: the attention kernel
-    reaches K/V through the block table instead of a contiguous copy ([OT]
-    "Block Tables and Sharing"; [AF] "PagedAttention").
+  * To the model the tokens remain one unbroken sequence; only the
+    addressing changes, the attention kernel following the block table
+    rather than reading a contiguous copy ([OT] "Block Tables and Sharing";
+    [AF] "PagedAttention").
   * Decoding attends the new token's query over the cached K/V of the tokens
     already processed ([AF] "What the KV cache actually is").
 

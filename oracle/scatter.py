@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-The pages say a sequence grows by claiming one free physical block at a time,
-without relocating earlier blocks ([OT] "Answer Key", question 2), and that a
-block table maps logical position to physical block ([UD] intro).  The step
+Per the pages, a growing sequence takes free blocks one by one and its
+earlier blocks never move ([OT] "Answer Key", question 2), and a block table
+maps each logical position to a physical block ([UD] intro).  The step
 that puts a freshly computed token into that pool is not spelled out there;
 the reading taken here is the plainest one: a token's slot is
 

@@ -4,11 +4,12 @@
 // Follows "AI Engineering Visualised: KV cache" (intro: blocks are handed out
 // only as a sequence grows), the "Paged KV Cache" tutorial (sections "Block
 // Tables and Sharing": a block returns to the free list once nothing
-// references it, refcounted prefix sharing with a fresh block only when
-// sequences diverge inside a shared tail block; "Internal Fragmentation":
-// only the last block is partly empty; "Answer Key" question 2: growth claims
-// one free block at a time without relocating earlier ones) and "KV cache and
-// PagedAttention in serving" ("The bonus: sharing via copy-on-write").
+// references it, prefix blocks shared by reference count, and a block of
+// its own for a sequence that appends into a shared, partly filled last
+// block; "Internal Fragmentation": only the last block is partly empty;
+// "Answer Key" question 2: a growing sequence takes free blocks one by one
+// and its earlier blocks never move) and "KV cache and PagedAttention in
+// serving" ("The bonus: sharing via copy-on-write").
 //
 // The FIFO order, the all-or-nothing append and the (src, dst) report of a
 // copy-on-write are this library's policy; the declarations in pkv.h state it.

@@ -55,8 +55,10 @@
 //   XOR-swizzled by the row to spread banks), and one transposing LDS read
 //   (ds_read_b64_tr_b16) per 16 rows of d returns the 4 tokens x 1 d cell
 //   each lane needs.  The probabilities are split into a hi and a lo 16-bit
-//   part (p = hi + lo + O(2^-16 p)) and applied by two v_mfma_f32_16x16x16
-//   per 16 rows of d, so P keeps ~16 bits of precision.
+//   part (p = hi + lo + O(2^-16 p)) and applied by one v_mfma_f32_16x16x32
+//   per 16 rows of d whose contraction takes each token twice, with its hi
+//   and its lo part, so P keeps ~16 bits of precision at the MFMA count of a
+//   single 16-bit P.
 //   FP8 (OCP E4M3) K/V are converted in registers by the hardware converter
 //   (exact into bf16/f16); k_scale folds into the logit scale and v_scale
 //   into the final normalisation.
@@ -642,17 +644,6 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
-template <int CT>
-__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
-  if constexpr (CT == kBF16) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b),
-                                                     c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
-                                                 0, 0);
-  }
-}
-
 // Issue spacing after a group of MFMAs.  With the toolchain in use, vector
 // instructions that overwrote a source register of a v_mfma_f32_16x16x32 (its
 // A operand or its accumulator input; 8 passes on gfx950) a few instructions
@@ -1052,8 +1043,12 @@ decode_mfma_kernel(Params p) {
         }
       }
 
-      // 4) O^T += V^T P^T: per 16 rows of d, two 16x16x16 MFMAs (hi and lo
-      //    parts of P) whose A operand is the 8-byte V^T cell of 4 tokens
+      // 4) O^T += V^T P^T: per 16 rows of d, one 16x16x32 MFMA whose
+      //    contraction runs over the tile's 16 tokens twice, once with the hi
+      //    and once with the lo part of P: the 8 contraction slots of lane
+      //    group q4 are (tokens 4 q4 .. 4 q4 + 3, hi) then (the same tokens,
+      //    lo), so its A operand is the 8-byte V^T cell of those 4 tokens
+      //    twice and its B operand the hi cell followed by the lo cell
       // A operands by transposing reads: lane (4k + m) of each 16-lane group
       // points at 4 elements d = 16n + 4m .. +3 of token 4*q4 + k, and lane j
       // receives element j of those 4 tokens' rows, i.e. V^T[16n + j][4*q4 .. +3]
@@ -1072,10 +1067,10 @@ decode_mfma_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
+        const u32x4 pb = u32x4{p_hi[k][0], p_hi[k][1], p_lo[k][0], p_lo[k][1]};
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[k][n] = mfma_16x16x16<CT>(cell[n], p_hi[k], acc[k][n]);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[k][n] = mfma_16x16x16<CT>(cell[n], p_lo[k], acc[k][n]);
+        for (int n = 0; n < NT; ++n)
+          acc[k][n] = mfma_16x16x32<CT>(u32x4{cell[n][0], cell[n][1], cell[n][0], cell[n][1]}, pb, acc[k][n]);
       }
       mfma_guard();
       compiler_fence();

@@ -1,8 +1,9 @@
 // reshape_and_cache: write each new token's K and V into its slot of the
 // paged pool, for gfx950.
 //
-// A sequence grows by claiming free blocks without relocating earlier ones
-// ("Paged KV Cache" tutorial, section "Answer Key", question 2), so the new
+// A growing sequence takes free blocks one by one and its earlier blocks
+// never move ("Paged KV Cache" tutorial, section "Answer Key", question 2),
+// so the new
 // token of a decode step writes exactly one slot: slot = block * B + offset,
 // landing at cache[slot / B, head, slot % B, :].
 //

@@ -75,19 +75,19 @@ def test_equal_keys_give_the_mean_of_v(q, kv, new, bs):
     c = _case(q, kv, new, bs, 83)
     print(f"[case] {c.wl.name} equal keys", flush=True)
     wl = c.wl
-    # one key row per KV head, copied into every slot of the pool and into
-    # the new tokens (an FP8 pool takes the code the scatter would store)
-    kc = c.t.k_cache
-    row = kc[0, :, 0, :].clone()                              # a stored row of each head
-    kc.copy_(row[None, :, None, :].expand_as(kc))
-    if wl.kv_dtype == "fp8":
-        key = (row.view(torch.float8_e4m3fn).float() * c.t.k_scale).to(c.t.new_k.dtype)
-    else:
-        key = row.to(c.t.new_k.dtype)
-    c.t.new_k.copy_(key[None].expand_as(c.t.new_k))
+    # every sequence's new token takes the key of the first one; the scatter
+    # stores that one row (bits, or the FP8 codes it rounds to) in every new
+    # token's slot, and the row is then copied into every slot of the pool
+    c.t.new_k.copy_(c.t.new_k[:1].expand_as(c.t.new_k))
     c.scatter()
-    assert torch.equal(c.t.k_cache, kc) and torch.equal(kc, row[None, :, None, :].expand_as(kc)), \
-        "the scatter stored another key"
+    s0 = next(s for s, ctx in enumerate(c.plan.context_lens.tolist()) if ctx >= 1)
+    slot = int(c.rp.slot_mapping[s0])
+    kc = c.t.k_cache
+    row = kc[slot // wl.block_size, :, slot % wl.block_size, :].clone()   # [Hkv, D] as stored
+    for sl in c.rp.slot_mapping.tolist():
+        if sl >= 0:
+            assert torch.equal(kc[sl // wl.block_size, :, sl % wl.block_size, :], row), "new tokens differ"
+    kc.copy_(row[None, :, None, :].expand_as(kc))
     out = c.decode()
     torch.cuda.synchronize()
     ref = c.oracle_decode()

@@ -22,17 +22,16 @@ def test_bytes_per_token(pages_capacity):
 def test_twelve_gib_pool(pages_capacity):
     bpt = cap.kv_bytes_per_token(80, 8, 128, 2)
     assert GIB12 == pages_capacity["budget_bytes"]
-    assert cap.token_slots(GIB12, bpt) == pages_capacity["token_slots_12gib"]
-    blocks = cap.pool_blocks(GIB12, bpt, 16)
-    assert blocks == pages_capacity["pool_blocks_12gib_b16"]
-    assert blocks * 16 == pages_capacity["block_backed_slots_12gib_b16"]
-    left = cap.leftover_bytes(GIB12, bpt, 16)
-    assert left == pages_capacity["leftover_bytes_12gib_b16"]
-    assert round(left / bpt, 1) == 9.6
+    pool = cap.carve(GIB12, bpt, 16)
+    assert pool.token_slots == pages_capacity["token_slots_12gib"]
+    assert pool.blocks == pages_capacity["pool_blocks_12gib_b16"]
+    assert pool.block_slots == pages_capacity["block_backed_slots_12gib_b16"]
+    assert pool.leftover_bytes == pages_capacity["leftover_bytes_12gib_b16"]
+    assert round(pool.leftover_bytes / bpt, 1) == 9.6
 
 
 def test_825_token_request(pages_capacity):
-    r = cap.paged_request(825, 16, reserved_tokens=2048)
+    r = cap.footprint(825, 16, reserved_tokens=2048)
     assert r.blocks == pages_capacity["request_825_blocks_b16"]
     assert r.slots == pages_capacity["request_825_slots_b16"]
     assert r.unused_slots == pages_capacity["request_825_unused_b16"]
@@ -44,29 +43,28 @@ def test_825_token_request(pages_capacity):
 
 def test_request_capacity(pages_capacity):
     bpt = cap.kv_bytes_per_token(80, 8, 128, 2)
-    slots = cap.token_slots(GIB12, bpt)
-    blocks = cap.pool_blocks(GIB12, bpt, 16)
-    per_req = cap.paged_request(825, 16).blocks
-    contiguous = cap.contiguous_requests(slots, 2048)
-    paged = cap.paged_requests(blocks, per_req)
+    pool = cap.carve(GIB12, bpt, 16)
+    contiguous = cap.contiguous_admissions(pool.token_slots, 2048)
+    paged = cap.paged_admissions(pool.blocks, 16, 825)
     assert contiguous == pages_capacity["contiguous_requests_825_of_2048"]
     assert paged == pages_capacity["paged_requests_825"]
     assert round(paged / contiguous, 4) == pages_capacity["capacity_ratio_825"]
-    need48 = 48 * cap.paged_request(825, 16).slots
+    need48 = 48 * cap.footprint(825, 16).slots
     assert need48 == pages_capacity["slots_for_48_requests_825"]
-    assert need48 > blocks * 16  # the 48th request does not fit
+    assert need48 > pool.block_slots  # the 48th request does not fit
 
 
 def test_fp8_and_broken_cases(pages_capacity):
-    assert cap.token_slots(GIB12, cap.kv_bytes_per_token(80, 8, 128, 1)) == pages_capacity["token_slots_12gib_fp8"]
-    assert cap.paged_request(825, 32).blocks == pages_capacity["request_825_blocks_b32"]
-    assert cap.paged_request(825, 32).slots == cap.paged_request(825, 16).slots
-    assert cap.paged_request(200, 16).slots == pages_capacity["request_200_slots_b16"]
-    assert cap.paged_request(200, 32).slots == pages_capacity["request_200_slots_b32"]
-    wrong = cap.token_slots(GIB12, cap.kv_bytes_per_token(80, 64, 128, 2))
-    assert wrong == pages_capacity["token_slots_12gib_64_heads"]
-    # "4-5x" is not what this workload gives
-    assert not 4.0 <= 2048 / cap.paged_request(825, 16).slots <= 5.0
+    fp8 = cap.carve(GIB12, cap.kv_bytes_per_token(80, 8, 128, 1), 16)
+    assert fp8.token_slots == pages_capacity["token_slots_12gib_fp8"]
+    assert cap.footprint(825, 32).blocks == pages_capacity["request_825_blocks_b32"]
+    assert cap.footprint(825, 32).slots == cap.footprint(825, 16).slots
+    assert cap.footprint(200, 16).slots == pages_capacity["request_200_slots_b16"]
+    assert cap.footprint(200, 32).slots == pages_capacity["request_200_slots_b32"]
+    wrong = cap.carve(GIB12, cap.kv_bytes_per_token(80, 64, 128, 2), 16)
+    assert wrong.token_slots == pages_capacity["token_slots_12gib_64_heads"]
+    # a 4-5x allocation ratio is not what this workload gives
+    assert not 4.0 <= 2048 / cap.footprint(825, 16).slots <= 5.0
 
 
 def test_prefix_granularity(pages_capacity):
@@ -84,20 +82,21 @@ def test_other_pages_examples(pages_capacity):
     assert abs(gqa - approx) / approx < 0.10
     approx8k = pages_capacity["approx_70b_gqa_bytes_8000_tokens"]
     assert abs(8000 * gqa - approx8k) / approx8k < 0.10
-    # "the 8B preset costs a quarter of the no-GQA 7B": 8 vs 32 KV heads
+    # the 8B GQA preset against the 7B model without GQA ([UD] "The maths"):
+    # 8 against 32 KV heads, a quarter of the bytes
     assert cap.kv_bytes_per_token(32, 8, 128, 2) * 4 == cap.kv_bytes_per_token(32, 32, 128, 2)
 
 
 @pytest.mark.parametrize("tokens,block,reserved", [(0, 16, 2048), (-5, 16, 2048), (10, 0, 2048), (3000, 16, 2048)])
 def test_invalid_inputs_rejected(tokens, block, reserved):
     with pytest.raises(ValueError):
-        cap.paged_request(tokens, block, reserved_tokens=reserved)
+        cap.footprint(tokens, block, reserved_tokens=reserved)
 
 
 def test_tail_waste_bound_exhaustive():
     # only the final block can be partly empty: waste <= block_size - 1
     for bs in (1, 2, 3, 16, 32):
         for n in range(1, 400):
-            r = cap.paged_request(n, bs)
+            r = cap.footprint(n, bs)
             assert 0 <= r.unused_slots <= bs - 1
             assert r.slots - bs < n <= r.slots
