@@ -159,6 +159,32 @@ pkv_status pkv_paged_attention_decode_splits(void* out, pkv_dtype out_dtype,
                                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid allocation): the
+ * same computation, bits and arguments as pkv_paged_attention_decode, with
+ * no workspace argument.  The library uses its own workspace instead, a
+ * device array of 64 MiB that each GPU the library runs on holds from the
+ * first such call until the process ends; the call allocates nothing.
+ * Its counters take at most 65,536 (sequence, KV head) pairs, and the
+ * partial states of the split over blocks must fit the rest of the array
+ * (about num_seqs * h_q * splits * (head_dim + 2) * 4 bytes, splits being
+ * the library's choice); larger calls return PKV_EWORKSPACE before any
+ * launch.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (on different streams, or from different threads)
+ * race and give undefined results.  The first call on each GPU also clears
+ * the counters with a small kernel on `stream`.
+ * Errors: as for pkv_paged_attention_decode.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_paged_attention_decode_noalloc(void* out, pkv_dtype out_dtype,
+                                              const void* q, pkv_dtype q_dtype,
+                                              const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                              float k_scale, float v_scale,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                                              int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                              float scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * One decode step in one launch: each sequence's new token is written into
  * its slot and attention runs over the context that includes it.
  *

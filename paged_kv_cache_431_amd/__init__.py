@@ -75,6 +75,7 @@ def lib():
         "pkv_decode_num_splits": (c_int, [c_int] * 7),
         "pkv_paged_attention_decode": (c_int, _DECODE_ARGS),
         "pkv_paged_attention_decode_splits": (c_int, _DECODE_ARGS[:20] + [c_int] + _DECODE_ARGS[20:]),
+        "pkv_paged_attention_decode_noalloc": (c_int, _DECODE_ARGS[:20] + _DECODE_ARGS[22:]),
         "pkv_decode_step": (c_int, _STEP_ARGS),
         "pkv_decode_step_splits": (c_int, _STEP_ARGS[:23] + [c_int] + _STEP_ARGS[23:]),
         "pkv_multi_workspace_bytes": (c_sz, [c_int] * 8),
@@ -166,8 +167,8 @@ def make_workspace(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, n
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, workspace, scale, k_scale,
                  v_scale, num_splits, stream):
     """Checked, marshalled arguments of pkv_paged_attention_decode (num_splits
-    == 0) or pkv_paged_attention_decode_splits (num_splits inserted after
-    scale)."""
+    == 0), pkv_paged_attention_decode_splits (num_splits inserted after
+    scale) or, with workspace None, pkv_paged_attention_decode_noalloc."""
     import torch
     S, h_q, D = q.shape
     NB, h_kv, B, D2 = k_cache.shape
@@ -180,12 +181,13 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_tables must be [S, MB] and context_lens [S]")
     split_arg = (int(num_splits),) if num_splits else ()
+    ws_arg = () if workspace is None else (_dev_ptr(workspace, "workspace"),
+                                           workspace.numel() * workspace.element_size())
     return (_dev_ptr(out, "out"), dtype_code(out), _dev_ptr(q, "q"), dtype_code(q),
             _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), dtype_code(k_cache),
             float(k_scale), float(v_scale), _dev_ptr(block_tables, "block_tables"),
             _dev_ptr(context_lens, "context_lens"), S, h_q, h_kv, D, B, NB, block_tables.shape[1],
-            int(max_context_len), float(scale), *split_arg, _dev_ptr(workspace, "workspace"),
-            workspace.numel() * workspace.element_size(), _stream(stream))
+            int(max_context_len), float(scale), *split_arg, *ws_arg, _stream(stream))
 
 
 def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
@@ -203,6 +205,17 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
                         k_scale, v_scale, num_splits, stream)
     name = "pkv_paged_attention_decode_splits" if num_splits else "pkv_paged_attention_decode"
     _check(getattr(lib(), name)(*args), name)
+    return out
+
+
+def pkv_paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
+                                       scale=0.0, k_scale=1.0, v_scale=1.0, stream=None):
+    """pkv_paged_attention_decode without a workspace argument: the library
+    uses its own per-GPU workspace and allocates nothing (for callers that
+    cannot allocate).  Calls that overlap on one GPU race."""
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, None, scale, k_scale,
+                        v_scale, 0, stream)
+    _check(lib().pkv_paged_attention_decode_noalloc(*args), "pkv_paged_attention_decode_noalloc")
     return out
 
 

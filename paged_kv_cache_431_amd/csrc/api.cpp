@@ -149,7 +149,7 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
                          float v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                          int h_q, int h_kv, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                          int max_context_len, float scale, int num_splits, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool own_workspace = false) {
   const bool multi = query_start != nullptr;
   const bool append = new_k != nullptr;
   if (!decode_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_context_len, num_splits)) return PKV_EINVAL;
@@ -157,7 +157,8 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_EINVAL;
   if (!valid_dtype(out_dtype) || !valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PKV_EINVAL;
   if (num_seqs == 0 || (multi && num_query_tokens == 0)) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace) return PKV_EINVAL;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_EINVAL;
+  if (!own_workspace && !workspace) return PKV_EINVAL;
   if (!(std::isfinite(scale))) return PKV_EINVAL;
   if (kv_dtype == PKV_FP8_E4M3 && !(k_scale > 0.f && std::isfinite(k_scale) && v_scale > 0.f && std::isfinite(v_scale)))
     return PKV_EINVAL;
@@ -197,9 +198,19 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
   if (balanced > 0 && (int64_t)num_seqs * h_kv *
                               ceil_div((int64_t)max_blocks_per_seq * block_size, pkv::kTileTokens) >= INT32_MAX)
     balanced = 0;
-  const pkv::WorkspaceLayout L = multi ? pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n)
-                                       : pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n, balanced);
-  if (workspace_bytes < L.total) return PKV_EWORKSPACE;
+  // the library's own workspace (decode only) keeps a counters region of
+  // fixed capacity, so that no call's partial states overlap another's counters
+  const int counter_slots = own_workspace ? pkv::kStaticCounterSlots : 0;
+  if (own_workspace && (multi || (int64_t)num_seqs * h_kv > counter_slots)) return PKV_EWORKSPACE;
+  const pkv::WorkspaceLayout L =
+      multi ? pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n)
+            : pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n, balanced, counter_slots);
+  if (own_workspace) {
+    if (L.total > pkv::kStaticWorkspaceBytes) return PKV_EWORKSPACE;
+    if (pkv::static_workspace(stream, &workspace) != hipSuccess) return PKV_EHIP;
+  } else if (workspace_bytes < L.total) {
+    return PKV_EWORKSPACE;
+  }
 
   const double s = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)head_dim);
   const double log2e = 1.4426950408889634;
@@ -237,6 +248,7 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
   a.k_scale_enc = k_scale;
   a.v_scale_enc = v_scale;
   a.balanced_workgroups = balanced;
+  a.counter_slots = counter_slots;
   // resident workgroups per SIMD: 2 for the kernels holding two row tiles
   const int waves_per_simd =
       multi && pkv::multi_tiles_per_workgroup(row_tiles) == 2 ? 2 : pkv::kDecodeWavesPerSimd;
@@ -325,6 +337,18 @@ pkv_status pkv_paged_attention_decode_splits(void* out, pkv_dtype out_dtype, con
                        k_scale, v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size,
                        num_blocks, max_blocks_per_seq, max_context_len, scale, num_splits, workspace,
                        workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_decode_noalloc(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                              const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                              float k_scale, float v_scale, const int32_t* block_tables,
+                                              const int32_t* context_lens, int num_seqs, int h_q, int h_kv,
+                                              int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                                              int max_context_len, float scale, hipStream_t stream) {
+  return run_attention(out, out_dtype, q, q_dtype, nullptr, 0, 1, nullptr, nullptr, 0, k_cache, v_cache, kv_dtype,
+                       k_scale, v_scale, block_tables, context_lens, num_seqs, h_q, h_kv, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, 0, nullptr, 0, stream,
+                       /*own_workspace=*/true);
 }
 
 namespace {

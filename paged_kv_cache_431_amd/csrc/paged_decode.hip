@@ -1396,7 +1396,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const int row_tiles = multi ? multi_row_tiles(a.h_q, a.h_kv, a.max_query_len) : 1;
   const WorkspaceLayout L = multi ? multi_workspace_layout(a.num_seqs, a.h_kv, a.head_dim, row_tiles, a.num_splits)
                                   : decode_workspace_layout(a.num_seqs, a.h_q, a.h_kv, a.head_dim, a.num_splits,
-                                                            a.balanced_workgroups);
+                                                            a.balanced_workgroups, a.counter_slots);
   Params p;
   p.out = a.out;
   p.q = a.q;

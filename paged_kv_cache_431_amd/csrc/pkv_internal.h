@@ -68,6 +68,10 @@ struct DecodeLaunch {
   // sequences are taken in decreasing order of their tile count shifted
   // right by this many bits (ties in index order).
   int lpt_shift = -1;
+  // Counters region of the workspace, in int32 slots: 0 sizes it for this
+  // call's units; a fixed capacity (the library's own workspace) keeps the
+  // partial states of every call clear of the counters of any other.
+  int counter_slots = 0;
 };
 
 // 16-row tiles of (query token, query head) rows per (sequence, KV head).
@@ -95,8 +99,20 @@ struct WorkspaceLayout {
 
 // balanced_workgroups > 0: the layout of balanced ranges (two partial-state
 // slots per workgroup) instead of one per (sequence, KV head, split).
+// counter_slots > 0: a counters region of that many int32 slots (at least the
+// call's units) instead of one sized for the call.
 WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits,
-                                        int balanced_workgroups = 0);
+                                        int balanced_workgroups = 0, int counter_slots = 0);
+
+// The library's own decode workspace for callers that cannot allocate: a
+// file-scope device array of kStaticWorkspaceBytes per GPU, whose first
+// kStaticCounterSlots int32 slots are the counters (zeroed once, on the
+// first use on each device, by a fill kernel on `stream`; every call leaves
+// them zero) and the rest the partial states.  *ptr receives this device's
+// address of the array.
+constexpr size_t kStaticWorkspaceBytes = size_t(64) << 20;
+constexpr int kStaticCounterSlots = 1 << 16;
+hipError_t static_workspace(hipStream_t stream, void** ptr);
 
 // Workspace of a call with several query tokens per sequence: one counter
 // and 16 partial-state rows per split for each (sequence, KV head, row tile),

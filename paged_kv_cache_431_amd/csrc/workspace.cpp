@@ -6,7 +6,7 @@
 namespace pkv {
 
 WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int head_dim, int num_splits,
-                                        int balanced_workgroups) {
+                                        int balanced_workgroups, int counter_slots) {
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t units = (size_t)num_seqs * h_kv;
   const size_t rows = balanced_workgroups > 0
@@ -14,7 +14,7 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int hea
                           : (size_t)num_seqs * h_q * num_splits;           // units * G * splits
   WorkspaceLayout L;
   L.counters = 0;
-  L.ml = align(units * sizeof(int32_t));
+  L.ml = align((counter_slots > 0 ? (size_t)counter_slots : units) * sizeof(int32_t));
   L.acc = L.ml + align(rows * 2 * sizeof(float));
   L.total = L.acc + align(rows * head_dim * sizeof(float));
   return L;

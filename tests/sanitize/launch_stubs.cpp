@@ -21,4 +21,6 @@ hipError_t launch_copy_blocks(void*, void*, const void*, const void*, const int3
   return hipErrorInvalidDeviceFunction;
 }
 
+hipError_t static_workspace(hipStream_t, void**) { return hipErrorInvalidDeviceFunction; }
+
 }  // namespace pkv

@@ -185,6 +185,24 @@ def test_decode_rejects_bad_scalars_without_launching(over, status):
     assert _decode(**over) == status
 
 
+def test_noalloc_decode_rejects_without_launching():
+    """The no-alloc decode validates like decode, and refuses calls beyond
+    its own workspace before touching the GPU (the pointers are not real)."""
+    L = pkv.lib()
+    P = ctypes.c_void_p
+    call = lambda **o: L.pkv_paged_attention_decode_noalloc(
+        P(1), 0, P(o.get("q", 1)), 2, P(1), P(1), 2, 1.0, 1.0, P(1), P(1), o.get("S", 4), o.get("hq", 8),
+        o.get("hkv", 2), o.get("d", 128), 16, 10, o.get("mb", 4), o.get("maxctx", 64), 0.0, None)
+    assert call(q=None) == pkv.PKV_EINVAL
+    assert call(d=96) == pkv.PKV_EINVAL
+    assert call(hq=6, hkv=4) == pkv.PKV_EINVAL
+    assert call(S=0) == pkv.PKV_OK
+    assert call(S=40000, hq=8, hkv=2) == pkv.PKV_EWORKSPACE       # 80,000 (sequence, KV head) counters
+    # partial states beyond the array: 8,000 sequences x 64 heads split over
+    # 32,000-token contexts need far more than 64 MiB
+    assert call(S=8000, hq=64, hkv=8, mb=2000, maxctx=32000) == pkv.PKV_EWORKSPACE
+
+
 def _multi(**over):
     args = dict(out=1, out_dtype=0, q=1, q_dtype=2, qs=1, T=12, mql=4, k=1, v=1, kv=2, ks=1.0, vs=1.0, bt=1, cl=1,
                 S=4, hq=8, hkv=2, d=128, bs=16, nb=10, mb=4, maxctx=64, scale=0.0, splits=0, ws=1, wsb=1 << 30,
