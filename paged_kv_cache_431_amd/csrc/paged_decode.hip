@@ -520,16 +520,27 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
 
 // Balanced ranges (decode with long contexts over few (sequence, KV head)
 // pairs, where one workgroup per pair and split leaves the work uneven): the
-// tiles of all pairs, pair after pair in (sequence, KV head) order, are cut
-// into equal contiguous ranges, one per workgroup, so every workgroup reads
-// the same number of bytes whatever the mix of context lengths.  A range may
-// hold the end of one pair, whole pairs and the start of another: each is an
-// item of its own, run one after the other; the pieces of a pair split over
-// several workgroups meet through the workspace as splits do.
+// tiles of all pairs are cut into equal contiguous ranges, one per
+// workgroup, so every workgroup reads the same number of bytes whatever the
+// mix of context lengths.  A range may hold the end of one pair, whole pairs
+// and the start of another: each is an item of its own, run one after the
+// other; the pieces of a pair split over several workgroups meet through the
+// workspace as splits do.
+//
+// The pairs are laid out KV head by KV head (all sequences of head 0, then
+// of head 1, ...), and with a grid of 8k workgroups, range j of head block x
+// goes to a workgroup id with residue x mod 8: one XCD walks all pairs of
+// "its" heads.  Sequences that share prefix blocks (copy-on-write sharing)
+// then read them through one L2.  A range runs its items from the last to
+// the first, so the piece that starts a pair (its prefix) comes first:
+// every range walks its prefix at the start of the launch, and the sharers
+// of a prefix walk it at about the same time.
 struct Balanced {
   int S, H, cap;  // sequences, KV heads, context lengths taken at most this
+  int T_head;     // tiles of one KV head's pairs (every head has the same)
   int r;          // tiles per range (0: this workgroup has none)
-  int pos, end;   // this workgroup's next flattened tile and its range end
+  int w;          // this workgroup's range
+  int pos, end;   // its range [pos, end) still to run, items taken from the end
 };
 
 // pre (LDS, S + 1 entries) receives the prefix sums of the sequences' tile
@@ -571,49 +582,55 @@ __device__ void balanced_setup(const Params& p, int* pre, Balanced& b) {
     if (lane == 0) pre[0] = 0;
   }
   __syncthreads();
-  const int T = b.H * pre[S];  // every pair's tiles
+  b.T_head = pre[S];
+  const int T = b.H * b.T_head;  // every pair's tiles
   // ranges of at least kBalancedMinRange tiles: with short contexts the
-  // later workgroups get nothing
-  const int w_eff = T > 0 ? min((int)gridDim.x, (T + kBalancedMinRange - 1) / kBalancedMinRange) : 0;
+  // later ranges get nothing
+  const int W = (int)gridDim.x;
+  const int w_eff = T > 0 ? min(W, (T + kBalancedMinRange - 1) / kBalancedMinRange) : 0;
   b.r = w_eff > 0 ? (T + w_eff - 1) / w_eff : 0;
-  const int w = blockIdx.x;
-  b.pos = w < w_eff ? w * b.r : 0;
-  b.end = w < w_eff ? min(T, b.pos + b.r) : 0;
+  // range of this workgroup: consecutive ranges (one head's pairs) on one XCD
+  b.w = (W & 7) == 0 ? (int)(blockIdx.x & 7) * (W >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  b.pos = b.w < w_eff ? b.w * b.r : 0;
+  b.end = b.w < w_eff ? min(T, b.pos + b.r) : 0;
 }
 
-// The next item of this workgroup's range, false when the range is done.
+// The next item of this workgroup's range, taken from the range's end:
+// false when the range is done.
 __device__ bool balanced_next(const Params& p, const int* pre, Balanced& b, Item& it) {
-  if (b.pos >= b.end) return false;
-  const int H = b.H;
-  // the sequence whose pairs hold flattened tile pos: the last s with
-  // H pre[s] <= pos (sequences without tiles hold none)
+  if (b.end <= b.pos) return false;
+  const int last = b.end - 1;          // the item holds this flattened tile
+  const int h = last / b.T_head;       // its KV head
+  const int q = last - h * b.T_head;   // its tile among that head's pairs
+  // the sequence whose pair holds tile q: the last s with pre[s] <= q
+  // (sequences without tiles hold none)
   int lo = 0, hi = b.S - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (H * pre[mid] <= b.pos) lo = mid;
+    if (pre[mid] <= q) lo = mid;
     else hi = mid - 1;
   }
-  const int ts = pre[lo + 1] - pre[lo];  // > 0: pos lies in it
-  const int kvh = (b.pos - H * pre[lo]) / ts;
-  const int first = H * pre[lo] + kvh * ts;  // the pair's first flattened tile
+  const int ts = pre[lo + 1] - pre[lo];  // > 0: q lies in it
+  const int first = h * b.T_head + pre[lo];  // the pair's first flattened tile
+  const int begin = max(first, b.pos);
   it.s = lo;
-  it.kvh = kvh;
-  it.unit = lo * H + kvh;
+  it.kvh = h;
+  it.unit = lo * b.H + h;
   const int ctx = p.context_lens[lo];
   it.append = ctx >= 1 && ctx <= b.cap;
   it.ctx = ctx < 0 ? 0 : (ctx > b.cap ? b.cap : ctx);
   it.n_tiles = ts;
-  it.t_begin = b.pos - first;
-  it.t_end = min(ts, b.end - first);
+  it.t_begin = begin - first;
+  it.t_end = b.end - first;
   it.bal_r = b.r;
   it.bal_w0 = first / b.r;
   it.bal_p = first;
   it.n_splits_seq = (first + ts - 1) / b.r - it.bal_w0 + 1;
-  it.split = blockIdx.x - it.bal_w0;
+  it.split = b.w - it.bal_w0;
   it.rt = 0;
   it.m = 1;
   it.q0 = 0;
-  b.pos = first + it.t_end;
+  b.end = begin;
   return true;
 }
 
