@@ -191,7 +191,9 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
   const int row_tiles = multi ? pkv::multi_row_tiles(h_q, h_kv, max_query_len) : 1;
   const int row_groups = multi ? pkv::multi_row_groups(row_tiles) : 1;
   if ((int64_t)ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_groups * n > INT32_MAX) return PKV_EUNSUPPORTED;
-  int balanced = !multi && matrix_core ? balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits) : 0;
+  // balanced ranges: decode, and several query tokens whose rows of a pair
+  // fit one workgroup (one row group)
+  int balanced = matrix_core && row_groups == 1 ? balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits) : 0;
   // balanced ranges count every pair's tiles up to the table's capacity in an
   // int (a context may exceed max_context_len); otherwise one workgroup per
   // pair and split, whose layout the workspace size also covers
@@ -203,7 +205,7 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
   const int counter_slots = own_workspace ? pkv::kStaticCounterSlots : 0;
   if (own_workspace && (multi || (int64_t)num_seqs * h_kv > counter_slots)) return PKV_EWORKSPACE;
   const pkv::WorkspaceLayout L =
-      multi ? pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n)
+      multi ? pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n, balanced)
             : pkv::decode_workspace_layout(num_seqs, h_q, h_kv, head_dim, n, balanced, counter_slots);
   if (own_workspace) {
     if (L.total > pkv::kStaticWorkspaceBytes) return PKV_EWORKSPACE;
@@ -391,6 +393,10 @@ pkv_status pkv_decode_step_splits(void* out, pkv_dtype out_dtype, const void* q,
 int pkv_multi_num_splits(int num_seqs, int h_q, int h_kv, int head_dim, int block_size, int max_query_len,
                          int max_context_len, int num_splits) {
   if (!multi_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len, num_splits)) return 0;
+  if (pkv::multi_row_groups(pkv::multi_row_tiles(h_q, h_kv, max_query_len)) == 1) {
+    const int balanced = balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits);
+    if (balanced > 0) return (int)ceil_div(balanced, (int64_t)num_seqs * h_kv);  // workgroups per pair, on average
+  }
   return resolve_multi_splits(num_seqs, h_q, h_kv, max_query_len, max_context_len, num_splits);
 }
 
@@ -398,8 +404,13 @@ size_t pkv_multi_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, 
                                  int max_context_len, int num_splits) {
   if (!multi_shape_ok(num_seqs, h_q, h_kv, head_dim, block_size, max_query_len, max_context_len, num_splits)) return 0;
   const int n = resolve_multi_splits(num_seqs, h_q, h_kv, max_query_len, max_context_len, num_splits);
-  return pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, pkv::multi_row_tiles(h_q, h_kv, max_query_len), n)
-      .total;
+  const int row_tiles = pkv::multi_row_tiles(h_q, h_kv, max_query_len);
+  // enough for either assignment (balanced ranges are taken on the
+  // matrix-core path with one row group only)
+  const int balanced =
+      pkv::multi_row_groups(row_tiles) == 1 ? balanced_workgroups(num_seqs, h_kv, max_context_len, num_splits) : 0;
+  return std::max(pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n).total,
+                  pkv::multi_workspace_layout(num_seqs, h_kv, head_dim, row_tiles, n, balanced).total);
 }
 
 pkv_status pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,

@@ -467,14 +467,14 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
   }
   const size_t base = (size_t)cidx * p.num_splits * R + g;  // partial row of split 0
   // partial row of piece sp: split sp of the pair, or with balanced ranges
-  // slot 0 (first item) or 1 (last item) of workgroup bal_w0 + sp: the pair
-  // is the first item of every workgroup after bal_w0, and of bal_w0 only if
-  // it starts where that workgroup's range starts
+  // slot 0 (first item) or 1 (last item) of range bal_w0 + sp, row tile k:
+  // the pair is the first item of every range after bal_w0, and of bal_w0
+  // only if it starts where that range starts
   auto prow_of = [&](int sp) -> size_t {
     if (it.bal_r > 0) {
       const int w = it.bal_w0 + sp;
       const int slot = (sp > 0 || it.bal_p == w * it.bal_r) ? 0 : 1;
-      return ((size_t)w * 2 + slot) * R + g;
+      return (((size_t)w * 2 + slot) * RT + k) * R + g;
     }
     return base + (size_t)sp * R;
   };
@@ -535,6 +535,23 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
 // the first, so the piece that starts a pair (its prefix) comes first:
 // every range walks its prefix at the start of the launch, and the sharers
 // of a prefix walk it at about the same time.
+// The query rows of sequence s for balanced ranges: one query token (decode),
+// or with several query tokens its rows [q0, q0 + m) of q and out, clamped
+// as get_item clamps them; every row of a pair is in one workgroup (its
+// tiles are the context's: the last row sees them all).
+__device__ __forceinline__ void query_rows(const Params& p, int s, Item& it) {
+  it.rt = 0;
+  it.m = 1;
+  it.q0 = 0;
+  if (p.query_start != nullptr) {
+    int q0 = p.query_start[s], q1 = p.query_start[s + 1];
+    q0 = min(max(q0, 0), p.num_query_tokens);
+    q1 = min(max(q1, q0), p.num_query_tokens);
+    it.q0 = q0;
+    it.m = min(q1 - q0, p.max_query_len);
+  }
+}
+
 struct Balanced {
   int S, H, cap;  // sequences, KV heads, context lengths taken at most this
   int T_head;     // tiles of one KV head's pairs (every head has the same)
@@ -627,15 +644,13 @@ __device__ bool balanced_next(const Params& p, const int* pre, Balanced& b, Item
   it.bal_p = first;
   it.n_splits_seq = (first + ts - 1) / b.r - it.bal_w0 + 1;
   it.split = b.w - it.bal_w0;
-  it.rt = 0;
-  it.m = 1;
-  it.q0 = 0;
+  query_rows(p, lo, it);
   b.end = begin;
   return true;
 }
 
 // Pairs of sequences without tiles (context 0) get zeros.
-template <int D>
+template <int D, bool MT, int RT>
 __device__ void balanced_zeros(const Params& p, const int* pre, const Balanced& b) {
   for (int u = blockIdx.x; u < p.units; u += gridDim.x) {
     const int s = u / b.H;
@@ -643,7 +658,9 @@ __device__ void balanced_zeros(const Params& p, const int* pre, const Balanced& 
       Item z;
       z.s = s;
       z.kvh = u - s * b.H;
-      write_zeros<D, false>(p, z, 0);
+      query_rows(p, s, z);
+#pragma unroll
+      for (int k = 0; k < RT; ++k) write_zeros<D, MT>(p, z, k);
     }
   }
 }
@@ -811,6 +828,9 @@ decode_mfma_kernel(Params p) {
     // row attends to.
     u32x4 qop[RT][NK];
     int row_lim[RT];
+    // several query tokens: every row attends to at least the positions
+    // [0, first_row_lim) (those of the first new token, ctx - m + 1)
+    const int first_row_lim = MT ? it.ctx - it.m + 1 : it.ctx;
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
       bool row_ok;
@@ -1001,9 +1021,14 @@ decode_mfma_kernel(Params p) {
         const int row_cut = MT ? min(lim, row_lim[k] - r.tok0) : lim;
         if constexpr (MT) {
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            s[rr] = sc[k][rr] * p.scale_log2;
-            if (4 * q4 + rr >= row_cut) s[rr] = kNegInf;
+          for (int rr = 0; rr < 4; ++rr) s[rr] = sc[k][rr] * p.scale_log2;
+          // wave-uniform: a whole tile before the first new token's position
+          // is seen by every row, so it skips the selects
+          if (partial || r.tok0 + kTileTokens > first_row_lim) {
+            asm volatile("");  // keeps this a branch instead of selects on every tile
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (4 * q4 + rr >= row_cut) s[rr] = kNegInf;
           }
         } else {
 #pragma unroll
@@ -1246,7 +1271,7 @@ decode_mfma_kernel(Params p) {
       run_item(it);
       __syncthreads();  // this item's merge is done with the LDS
     }
-    balanced_zeros<D>(p, sm_pre, bal);
+    balanced_zeros<D, MT, RT>(p, sm_pre, bal);
   }
 }
 
@@ -1381,6 +1406,11 @@ hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_
     if (!a.matrix_core || a.new_k != nullptr) return hipErrorInvalidValue;
     // one row group: this workgroup is the K/V's only reader
     const bool only_reader = p.row_groups == 1;
+    if (p.balanced) {  // balanced ranges hold every row of a pair: one row group
+      if (!only_reader) return hipErrorInvalidValue;
+      return multi_tiles_per_workgroup(p.row_tiles) == 2 ? dispatch_mfma<D, true, false, 2, true, true>(a, grid, p, s)
+                                                         : dispatch_mfma<D, true, false, 1, true, true>(a, grid, p, s);
+    }
     if (multi_tiles_per_workgroup(p.row_tiles) == 2) {
       return only_reader ? dispatch_mfma<D, true, false, 2, true>(a, grid, p, s)
                          : dispatch_mfma<D, true, false, 2, false>(a, grid, p, s);
@@ -1411,9 +1441,10 @@ hipError_t dispatch(const DecodeLaunch& a, int grid, const Params& p, hipStream_
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const bool multi = a.query_start != nullptr;
   const int row_tiles = multi ? multi_row_tiles(a.h_q, a.h_kv, a.max_query_len) : 1;
-  const WorkspaceLayout L = multi ? multi_workspace_layout(a.num_seqs, a.h_kv, a.head_dim, row_tiles, a.num_splits)
-                                  : decode_workspace_layout(a.num_seqs, a.h_q, a.h_kv, a.head_dim, a.num_splits,
-                                                            a.balanced_workgroups, a.counter_slots);
+  const WorkspaceLayout L =
+      multi ? multi_workspace_layout(a.num_seqs, a.h_kv, a.head_dim, row_tiles, a.num_splits, a.balanced_workgroups)
+            : decode_workspace_layout(a.num_seqs, a.h_q, a.h_kv, a.head_dim, a.num_splits, a.balanced_workgroups,
+                                      a.counter_slots);
   Params p;
   p.out = a.out;
   p.q = a.q;

@@ -116,8 +116,11 @@ hipError_t static_workspace(hipStream_t stream, void** ptr);
 
 // Workspace of a call with several query tokens per sequence: one counter
 // and 16 partial-state rows per split for each (sequence, KV head, row tile),
-// (sequence, KV head) pairs counted in whole groups of 8.
-WorkspaceLayout multi_workspace_layout(int num_seqs, int h_kv, int head_dim, int row_tiles, int num_splits);
+// (sequence, KV head) pairs counted in whole groups of 8; with balanced
+// ranges (balanced_workgroups > 0, one row group), one counter per (pair,
+// row tile) and two partial-state slots of 16 rows per row tile per range.
+WorkspaceLayout multi_workspace_layout(int num_seqs, int h_kv, int head_dim, int row_tiles, int num_splits,
+                                       int balanced_workgroups = 0);
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 

@@ -20,14 +20,16 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int h_q, int h_kv, int hea
   return L;
 }
 
-WorkspaceLayout multi_workspace_layout(int num_seqs, int h_kv, int head_dim, int row_tiles, int num_splits) {
+WorkspaceLayout multi_workspace_layout(int num_seqs, int h_kv, int head_dim, int row_tiles, int num_splits,
+                                       int balanced_workgroups) {
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   // one counter and 16 partial rows per split for every row tile the
   // workgroups hold (row groups x tiles per workgroup: one more than
   // row_tiles when an odd count is held two by two)
-  const size_t units = (((size_t)num_seqs * h_kv + 7) / 8) * 8 * multi_row_groups(row_tiles) *
-                       multi_tiles_per_workgroup(row_tiles);
-  const size_t rows = units * num_splits * 16;
+  const int per_wg = multi_tiles_per_workgroup(row_tiles);
+  const size_t units = (((size_t)num_seqs * h_kv + 7) / 8) * 8 * multi_row_groups(row_tiles) * per_wg;
+  const size_t rows = balanced_workgroups > 0 ? (size_t)balanced_workgroups * 2 * per_wg * 16  // two slots per range
+                                              : units * num_splits * 16;
   WorkspaceLayout L;
   L.counters = 0;
   L.ml = align(units * sizeof(int32_t));

@@ -9,7 +9,10 @@ workgroup) against the float64 oracle, through the C ABI:
   * 512 sequences of one KV head each (the most pairs the mode takes), so
     the prefix of tile counts spans many lanes;
   * repeated calls reuse the workspace (its counters return to zero);
-  * contexts longer than max_context_len are attended over in full.
+  * contexts longer than max_context_len are attended over in full;
+  * several new query tokens per sequence whose rows of a pair fit one
+    workgroup take balanced ranges too (one and two row tiles, ragged
+    token counts including none).
 """
 
 import numpy as np
@@ -112,3 +115,33 @@ def test_contexts_beyond_max_context_len_are_exact():
                                        num_splits=splits, workspace=ws)
         torch.cuda.synchronize()
         assert_close(out, ref, wl.kv_dtype, label=f"{wl.name}-splits{splits}")
+
+
+# several new query tokens per sequence whose rows of a pair fit one
+# workgroup (m x group <= 32): balanced ranges as for decode
+@pytest.mark.parametrize("kv,h_q,ms", [("bf16", 16, (1, 4, 2, 3, 0, 4, 1, 2, 4, 3)),     # group 8: two row tiles
+                                       ("fp8", 16, (4, 1, 3, 4, 4, 2, 1, 0, 3, 4)),
+                                       ("f16", 8, (1, 2, 4, 3, 4, 1, 2, 4, 0, 4)),       # group 4: one row tile
+                                       ("fp8", 4, (8, 1, 3, 8, 5, 2, 8, 1, 3, 6))])      # group 2, m up to 8
+def test_balanced_ranges_with_several_query_tokens(kv, h_q, ms):
+    wl = _wl(f"balanced-multi-{kv}-hq{h_q}", MIXED, kv=kv, h_q=h_q, seed=101)
+    max_m = max(ms)
+    assert max_m * wl.group <= 32
+    # the library takes balanced ranges for this call
+    assert pkv.pkv_multi_num_splits(wl.num_seqs, wl.h_q, wl.h_kv, wl.head_dim, wl.block_size, max_m,
+                                    max(MIXED)) > 3
+    print(f"[case] {wl.name} new={ms}", flush=True)
+    c = Case(wl)
+    c.scatter()
+    q, qs = workloads.multi_queries(wl, ms, device="cuda")
+    out = c.multi(q, qs, max_m)
+    torch.cuda.synchronize()
+    ref = c.oracle_multi(q, qs)
+    assert_close(out, ref, wl.kv_dtype, label=wl.name)
+    again = c.multi(q, qs, max_m)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), "a second call on the same workspace differs"
+    # one workgroup per pair and split: the same result within tolerance
+    forced = c.multi(q, qs, max_m, num_splits=3)
+    torch.cuda.synchronize()
+    assert_close(forced, ref, wl.kv_dtype, label=f"{wl.name}-splits3")
