@@ -1219,7 +1219,10 @@ decode_mfma_kernel(Params p) {
 #pragma unroll
         for (int b = 0; b < NBUF; ++b) {
           load_tile(buf[(b + NBUF - 1) % NBUF], i + b + NBUF - 1);
-          compute_tile(buf[b], i + b < cn);
+          // a ring step past the wave's last tile computes nothing (its
+          // loads read nothing); the kernels holding two row tiles measured
+          // faster computing it on zeros than branching around it
+          if (RT == 2 || i + b < cn) compute_tile(buf[b], i + b < cn);
         }
       }
     }
