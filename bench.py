@@ -60,9 +60,21 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("a3de61d715dec28fb21fec9071a31c4f7435321222906f065e42ad1661bf217a", "gqa70b-bf16-47x825-step", 1): 161759642,
-    ("a3de61d715dec28fb21fec9071a31c4f7435321222906f065e42ad1661bf217a", "gqa70b-bf16-47x825", 1): 161376256,
-    ("a3de61d715dec28fb21fec9071a31c4f7435321222906f065e42ad1661bf217a", "gqa70b-bf16-47x825-multi4", 1): 168386765,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-step", 1): 161772134,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825", 1): 161355776,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-multi4", 1): 168400896,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-b32-step", 1): 161733222,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-b32", 1): 161316864,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-b32-multi4", 1): 168361984,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa8b-bf16-256xU4096-step", 1): 2132192461,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa8b-bf16-256xU4096", 1): 2130027008,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa8b-bf16-256xU4096-multi4", 1): 2148944794,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "mha-f16-64x4096-step", 1): 4299453850,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "mha-f16-64x4096", 1): 4297264435,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "mha-f16-64x4096-multi4", 1): 4301997158,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "fp8-prefix-32xU32768-step", 2): 1305303347,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "fp8-prefix-32xU32768", 2): 1304438067,
+    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "fp8-prefix-32xU32768-multi4", 2): 1325145088,
 }
 
 
