@@ -297,6 +297,8 @@ def main():
     ap.add_argument("--copy-peak-mib", type=int, default=2048,
                     help="buffer size of the copy and sum that measure streaming rates (0 skips them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="before each timed group, launch its calls back to back for this long (GPU clocks settle)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB a few times (calibrates byte counters), then exit")
     args = ap.parse_args()
@@ -368,7 +370,21 @@ def main():
     layer_calls = steps_fused if fused else two_launch_calls
     kernel_calls = steps_fused if fused else decodes
 
+    def settle(calls):
+        # The GPU's clocks take a few milliseconds of load to settle after an
+        # idle gap (launch durations rise and fall again by up to 15 % over
+        # them in a kernel trace), so each timed group starts after its own
+        # calls have run back to back for settle_ms.  This is untimed.
+        t0 = time.perf_counter()
+        while True:
+            for call in calls:
+                call()
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= args.settle_ms:
+                return
+
     def time_step(calls):
+        settle(calls)
         for _ in range(args.warmup):
             for call in calls:
                 call()
@@ -396,6 +412,7 @@ def main():
     if fused:
         mean_launch_ms = ms_step / L
     else:
+        settle(kernel_calls)
         batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in batch:
             a.record(stream)
@@ -415,6 +432,7 @@ def main():
     launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
     decode_only_ms = mean_launch_ms
     if fused:  # the plain decode kernel over the same pools, for comparison
+        settle(decodes)
         batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in batch:
             a.record(stream)
@@ -440,7 +458,6 @@ def main():
     torch.cuda.synchronize()
     scatter_iso = sorted(a.elapsed_time(b) for a, b in sevs)
     pct = lambda xs, f: xs[min(len(xs) - 1, int(f * len(xs)))]
-    peaks = stream_peaks(dev, args.copy_peak_mib << 20) if args.copy_peak_mib else None
 
     per_call = kv_bytes_per_call(plan)
     step_bytes = per_call * L
@@ -453,6 +470,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -483,12 +501,7 @@ def main():
                      "isolated_launch_p10_us": round(pct(launch_ms, 0.1) * 1e3, 3),
                      "isolated_launch_p90_us": round(pct(launch_ms, 0.9) * 1e3, 3),
                      "isolated_launches": len(launch_ms),
-                     "measured_stream_peaks": (None if peaks is None else
-                                               {"copy_GBps": round(peaks[0], 1), "sum_GBps": round(peaks[1], 1),
-                                                "buffer_bytes": args.copy_peak_mib << 20,
-                                                "note": "device-to-device copy (read + write bytes) and float32 "
-                                                        "sum (bytes read) of one buffer, median of 10",
-                                                "achieved_over_sum": round(achieved / peaks[1], 4)}),
+                     "measured_stream_peaks": None,  # filled in last (below)
                      "algorithmic_bytes_per_launch": per_call,
                      "decode_only_mean_launch_us": round(decode_only_ms * 1e3, 3)},
     }
@@ -529,8 +542,7 @@ def main():
     multis = [pkv.prepare_paged_attention_multi(out_m, qm, t.k_cache, t.v_cache, tables, lens, qs_t, max_query_len=m,
                                                 max_context_len=plan.max_context_len, workspace=ws_m,
                                                 k_scale=t.k_scale, v_scale=t.v_scale, stream=stream) for t in pools]
-    for call in multis:
-        call()
+    settle(multis)
     batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in batch:
         a.record(stream)
@@ -549,6 +561,17 @@ def main():
         "kv_GBps": round(per_call / (multi_ms * 1e-3) / 1e9, 2),
         "frac_of_hbm_peak": round(per_call / (multi_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     result["swap_blocks"] = swap_measurement(pkv, pools[0], plan, wl, stream, n_pairs, HBM_PEAK_GBS)
+    # The plain-kernel stream rates come after every timing of the library's
+    # kernels: a 2 GiB copy and sum leave the GPU measurably slower for a
+    # while (a kernel timed right after them ran 5 % slower).
+    if args.copy_peak_mib:
+        peaks = stream_peaks(dev, args.copy_peak_mib << 20)
+        result["roofline"]["measured_stream_peaks"] = {
+            "copy_GBps": round(peaks[0], 1), "sum_GBps": round(peaks[1], 1),
+            "buffer_bytes": args.copy_peak_mib << 20,
+            "note": "device-to-device copy (read + write bytes) and float32 sum (bytes read) of one buffer, "
+                    "median of 10",
+            "achieved_over_sum": round(achieved / peaks[1], 4)}
     if not args.no_cpu_baseline:
         del pools, decodes, scatters, layer_calls, multis, steps_fused, two_launch_calls, kernel_calls
         torch.cuda.empty_cache()
