@@ -65,6 +65,12 @@ int balanced_workgroups(int num_seqs, int h_kv, int max_context_len, int num_spl
   return (int)std::min<int64_t>(kResidentWorkgroups, ceil_div(units * max_tiles, pkv::kBalancedMinRange));
 }
 
+// Workgroups of a decode launch with one workgroup per (sequence, KV head,
+// row group, split), the pairs counted in whole groups of 8.
+int64_t decode_grid(int num_seqs, int h_kv, int row_groups, int splits) {
+  return ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_groups * splits;
+}
+
 // Longest pairs first (the bin shift, or -1 for pairs in order): when a
 // decode grid of one workgroup per (sequence, KV head, split) does not fit on
 // the GPU at once, workgroups that start late should hold the short pairs.
@@ -72,13 +78,25 @@ int balanced_workgroups(int num_seqs, int h_kv, int max_context_len, int num_spl
 // kLptMaxSeqs sequences (every workgroup ranks them all).
 int longest_first_shift(int num_seqs, int h_kv, int max_context_len, int num_splits, int chosen_splits,
                         int row_groups, int waves_per_simd) {
-  const int64_t grid = ceil_div((int64_t)num_seqs * h_kv, 8) * 8 * row_groups * chosen_splits;
+  const int64_t grid = decode_grid(num_seqs, h_kv, row_groups, chosen_splits);
   if (num_splits > 0 || num_seqs > pkv::kLptMaxSeqs || grid <= (int64_t)pkv::kComputeUnits * waves_per_simd)
     return -1;
   const int64_t max_tiles = ceil_div(std::max(max_context_len, 0), pkv::kTileTokens);
   int shift = 0;
   while ((max_tiles >> shift) >= pkv::kLptBins) ++shift;
   return shift;
+}
+
+// The kernels with an LDS ring for K/V (one row tile, 16-bit caches, rows of
+// 128 elements, no balanced ranges).  Their ring takes 64 KiB of LDS per
+// workgroup, so two workgroups share a CU instead of three: they are taken
+// only for grids that need several rounds at three per CU, where they
+// measured faster (8B mixed-length and MHA batches, 2,048 workgroups); on a
+// grid resident in one round the register ring measured as fast or faster.
+bool lds_ring_fits(bool matrix_core, int balanced, int kv_dtype, int head_dim, bool multi, int row_tiles) {
+  const bool one_row_tile = !multi || pkv::multi_tiles_per_workgroup(row_tiles) == 1;
+  return matrix_core && balanced == 0 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_F16) && head_dim == 128 &&
+         one_row_tile;
 }
 
 int resolve_splits(int num_seqs, int h_kv, int max_context_len, int num_splits) {
@@ -257,6 +275,8 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
   a.lpt_shift = matrix_core && balanced == 0 ? longest_first_shift(num_seqs, h_kv, max_context_len, num_splits, n,
                                                                    row_groups, waves_per_simd)
                                              : -1;
+  a.lds_ring = lds_ring_fits(matrix_core, balanced, kv_dtype, head_dim, multi, row_tiles) &&
+               decode_grid(num_seqs, h_kv, row_groups, n) > (int64_t)pkv::kComputeUnits * pkv::kDecodeWavesPerSimd;
   const hipError_t e = pkv::launch_decode(a, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

@@ -101,6 +101,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;
@@ -733,6 +734,29 @@ __device__ __forceinline__ uint32_t kv_load4(__amdgpu_buffer_rsrc_t r, int lane_
   return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, off, STREAM ? 2 : 0);
 }
 
+// One 16-byte-per-lane buffer load straight into LDS: lane l's 16 bytes land
+// at LDS byte address lds + 16 l; bytes past the resource's size arrive as
+// zeros.  Written as assembly, so that the compiler, which does not model
+// which LDS bytes such a load writes, adds no wait of its own: the kernel
+// waits for these loads itself (s_waitcnt vmcnt) before reading their LDS.
+// The instruction has no register results.
+template <bool NT>
+__device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t lds, int lane_off, int off) {
+  if constexpr (NT) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(lds), "v"(lane_off), "s"(rsrc), "s"(off) : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(lane_off), "s"(rsrc), "s"(off) : "memory", "m0");
+  }
+}
+
+// A raw buffer resource over [base, base + bytes) as four words (for assembly).
+__device__ __forceinline__ i32x4 raw_rsrc(const uint8_t* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), bytes, kBufferWord3};
+}
+
 template <int KV, int D>
 struct MfmaTile {
   static constexpr int ES = KV == kFP8 ? 1 : 2;  // bytes per cached element
@@ -766,9 +790,14 @@ struct MfmaTile {
 // only walk of each (sequence, KV head)); false when several workgroups walk
 // the same K/V and share it through L2.  BAL: balanced ranges (decode only;
 // at most two workgroups per CU, so 2 waves per SIMD and their registers).
-template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM, bool BAL, bool LPT>
-__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(RT == 1 && !BAL ? kDecodeWavesPerSimd : 2))) void
+// DMA: K/V tiles (16-bit, 256-byte rows, one row tile) come straight into an
+// LDS ring instead of through registers; its 64 KiB per workgroup leave room
+// for two workgroups per CU.
+template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM, bool BAL, bool LPT, bool DMA>
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
+    RT == 1 && !BAL && !DMA ? kDecodeWavesPerSimd : 2))) void
 decode_mfma_kernel(Params p) {
+  static_assert(!DMA || (KV != kFP8 && D == 128 && RT == 1), "the LDS ring serves 16-bit rows of 256 bytes");
   using Tile = MfmaTile<KV, D>;
   constexpr int ROW = Tile::ROW;
   constexpr int KCH = Tile::KCH;
@@ -782,12 +811,20 @@ decode_mfma_kernel(Params p) {
     struct {
       // per-wave V tile of 16 tokens in its natural [token][d] layout, 16-bit
       // elements, 16-byte chunks of each row XOR-swizzled by the row
-      u32x4 vtile[kDecodeWaves][kTileTokens * VCH];
+      u32x4 vtile[kDecodeWaves][DMA ? 1 : kTileTokens * VCH];
       // decode step: the new token's K and V rows as stored in the pools, one
       // copy per wave (each wave stages its own: no barrier)
       uint8_t newrow[kDecodeWaves][2][ROW];
       // per-wave K tile: row t, 16-byte chunk c at byte t * KLDS + 16 c
-      u32x4 ktile[kDecodeWaves][kTileTokens * Tile::KLDS / 16];
+      u32x4 ktile[kDecodeWaves][DMA ? 1 : kTileTokens * Tile::KLDS / 16];
+      // LDS ring of the direct loads: per wave and ring stage, the K tile
+      // (row t, chunk c at chunk c ^ (t & 7) of row t) and the V tile (the
+      // layout of vtile)
+      u32x4 dk[kDecodeWaves][DMA ? NBUF : 1][DMA ? kTileTokens * VCH : 1];
+      u32x4 dv[kDecodeWaves][DMA ? NBUF : 1][DMA ? kTileTokens * VCH : 1];
+      // decode step with direct loads: the new token's K and V rows as given
+      // (16 bytes per lane land in lane order)
+      u32x4 nraw[kDecodeWaves][2][DMA && AP ? 64 : 1];
     } t;
     MergeSmem<D> merge;
     int lpt[kLptBins + 8];  // longest pairs first: bins and scan partials (before the walk)
@@ -858,8 +895,22 @@ decode_mfma_kernel(Params p) {
     // the new token's rows converted to the pool's element type, into the
     // owner wave's LDS copy (K row, then V row)
     auto stage_new_token = [&]() {
-      const c8_u32x4 nraw0 = {kx[0][0] | vx[0][0], kx[0][1] | vx[0][1], kx[1][0] | vx[1][0], kx[1][1] | vx[1][1]};
-      const c8_u32x4 nraw1 = {kx[2][0] | vx[2][0], kx[2][1] | vx[2][1], kx[3][0] | vx[3][0], kx[3][1] | vx[3][1]};
+      c8_u32x4 nraw0, nraw1;
+      if constexpr (DMA) {
+        // called at an owner's tile after its wait, when only the next
+        // tile's loads are in flight: the rows' direct loads, issued before
+        // those, have landed
+        const int es = p.new_dtype == kF32 ? 4 : (p.new_dtype == kFP8 ? 1 : 2);
+        const bool is_v = lane >= CH;
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(sm.t.nraw[wave][is_v ? 1 : 0]) +
+                             (is_v ? lane - CH : lane) * 8 * es;
+        const bool mine = lane < 2 * CH;
+        nraw0 = mine ? *reinterpret_cast<const c8_u32x4*>(src) : c8_u32x4{0u, 0u, 0u, 0u};
+        nraw1 = mine && es == 4 ? *reinterpret_cast<const c8_u32x4*>(src + 16) : c8_u32x4{0u, 0u, 0u, 0u};
+      } else {
+        nraw0 = c8_u32x4{kx[0][0] | vx[0][0], kx[0][1] | vx[0][1], kx[1][0] | vx[1][0], kx[1][1] | vx[1][1]};
+        nraw1 = c8_u32x4{kx[2][0] | vx[2][0], kx[2][1] | vx[2][1], kx[3][0] | vx[3][0], kx[3][1] | vx[3][1]};
+      }
       if (lane < 2 * CH) {
         const bool is_v = lane >= CH;
         uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][(is_v ? lane - CH : lane) * 8 * Tile::ES];
@@ -914,6 +965,15 @@ decode_mfma_kernel(Params p) {
     const uint8_t* v_head = p.v_cache + it.kvh * head_bytes;
     const int k_lane = lane * 16;                           // K: 16 bytes of each 1 KiB piece
     const int v_lane = (4 * q4) * ROW + lo16 * Tile::VB;    // V: row 4 q4 + rr, chunk lo16
+    // Direct loads: 1 KiB piece j of a tile (rows 4 j .. 4 j + 3) lands in
+    // LDS in lane order, lane (q4, lo16) at chunk lo16 of row 4 j + q4, so a
+    // lane reads the memory chunk whose swizzled place that is: K chunk
+    // lo16 ^ (row & 7), V chunk lo16 ^ ((row & 7) << 1); row & 7 is
+    // 4 (j & 1) + q4, so pieces 0, 2 and 1, 3 share an offset.
+    const int dk_even = q4 * ROW + ((lo16 ^ q4) << 4);
+    const int dk_odd = q4 * ROW + ((lo16 ^ q4 ^ 4) << 4);
+    const int dv_even = q4 * ROW + ((lo16 ^ (q4 << 1)) << 4);
+    const int dv_odd = q4 * ROW + ((lo16 ^ (q4 << 1) ^ 8) << 4);
 
     // Decode step: the wave whose tiles include the sequence's last position
     // (the last tile of the last split) appends the new token: it computes
@@ -923,38 +983,69 @@ decode_mfma_kernel(Params p) {
     const bool owner =
         AP && it.append && it.t_end == it.n_tiles && wb <= it.n_tiles - 1 && it.n_tiles - 1 < wb + n_my;
     const int last_tok0 = (it.n_tiles - 1) * kTileTokens;
+    const int stage_tok0 = min(wb + 1, it.n_tiles - 1) * kTileTokens;  // direct loads: where the owner stages
     int last_phys = -1;  // physical block of the last position (owner wave)
 
-    auto compute_tile = [&](Tile& r, bool valid) {
+    auto compute_tile = [&](Tile& r, bool valid, int stage) {
       const int lim = valid ? r.lim : 0;
-      // 0) K rows into the wave's LDS tile (lane l of load c holds chunk
-      //    l % LPR of row RPK c + l / LPR)
       uint8_t* kt = reinterpret_cast<uint8_t*>(sm.t.ktile[wave]);
+      u32x4* dks = sm.t.dk[wave][DMA ? stage : 0];
+      u32x4* dvs = sm.t.dv[wave][DMA ? stage : 0];
+      if constexpr (DMA) {
+        // this tile's direct loads are done when only the next tile's 8
+        // (issued after them) are in flight
+        static_assert(KCH == 4 && VDW == 4 && NBUF == 2, "direct loads: 4 K and 4 V loads per tile, one tile ahead");
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      } else {
+        // 0) K rows into the wave's LDS tile (lane l of load c holds chunk
+        //    l % LPR of row RPK c + l / LPR)
 #pragma unroll
-      for (int c = 0; c < KCH; ++c)
-        *reinterpret_cast<u32x4*>(kt + (Tile::RPK * c + lane / Tile::LPR) * Tile::KLDS + (lane % Tile::LPR) * 16) =
-            r.k[c];
+        for (int c = 0; c < KCH; ++c)
+          *reinterpret_cast<u32x4*>(kt + (Tile::RPK * c + lane / Tile::LPR) * Tile::KLDS + (lane % Tile::LPR) * 16) =
+              r.k[c];
+      }
+      if constexpr (AP && DMA) {
+        // the owner converts the new rows (loaded in its first chunk) into the
+        // pools' element type at its second tile, or its only one: the rows'
+        // loads came before that tile's, so they have landed, and the LDS
+        // work overlaps the ring instead of lengthening the last tile
+        if (owner && valid && r.tok0 == stage_tok0) stage_new_token();
+      }
       if constexpr (AP) {
         if (owner && valid && r.tok0 == last_tok0) {  // the tile holding the new token (wave-uniform)
           const int row = it.ctx - 1 - r.tok0;
-          if (lane < Tile::LPR) {
+          if constexpr (DMA) {
+            if (lane < 16) {
+              dks[16 * row + (lane ^ (row & 7))] = *reinterpret_cast<const u32x4*>(&sm.t.newrow[wave][0][lane * 16]);
+              dvs[16 * row + (lane ^ ((row & 7) << 1))] =
+                  *reinterpret_cast<const u32x4*>(&sm.t.newrow[wave][1][lane * 16]);
+            }
+          } else if (lane < Tile::LPR) {
             *reinterpret_cast<u32x4*>(kt + row * Tile::KLDS + lane * 16) =
                 *reinterpret_cast<const u32x4*>(&sm.t.newrow[wave][0][lane * 16]);
           }
+          if constexpr (!DMA) {
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            if (4 * q4 + rr == row) {
+            for (int rr = 0; rr < 4; ++rr) {
+              if (4 * q4 + rr == row) {
 #pragma unroll
-              for (int w = 0; w < VDW; ++w)
-                r.v[rr][w] = *reinterpret_cast<const uint32_t*>(&sm.t.newrow[wave][1][lo16 * Tile::VB + 4 * w]);
+                for (int w = 0; w < VDW; ++w)
+                  r.v[rr][w] = *reinterpret_cast<const uint32_t*>(&sm.t.newrow[wave][1][lo16 * Tile::VB + 4 * w]);
+              }
             }
           }
         }
       }
       // K in the operand layout: lane (lo16, q4) holds chunk q4 + 4 c of row lo16
       u32x4 kr[KCH];
+      if constexpr (DMA) {
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) kr[c] = *reinterpret_cast<const u32x4*>(kt + lo16 * Tile::KLDS + (q4 + 4 * c) * 16);
+        for (int c = 0; c < KCH; ++c) kr[c] = dks[16 * lo16 + ((q4 + 4 * c) ^ (lo16 & 7))];
+      } else {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+          kr[c] = *reinterpret_cast<const u32x4*>(kt + lo16 * Tile::KLDS + (q4 + 4 * c) * 16);
+      }
       // 1) scores for the 16 tokens of the tile against each (padded) row tile
       f32x4 sc[RT];
 #pragma unroll
@@ -974,9 +1065,11 @@ decode_mfma_kernel(Params p) {
       }
       mfma_guard();
 
-      // 2) V -> LDS in its natural layout; masked rows are zeroed first
+      // 2) V -> LDS in its natural layout; masked rows are zeroed first (the
+      //    direct loads put V there themselves, rows past the context as
+      //    zeros from the range check)
       const bool partial = lim < kTileTokens;
-      if (partial) {
+      if (!DMA && partial) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
           if (4 * q4 + rr >= lim) {
@@ -987,9 +1080,9 @@ decode_mfma_kernel(Params p) {
       // Row t of the tile, 16-byte chunk c sits at chunk c ^ swz(t) of row t:
       // the transposed reads below then touch all banks evenly.
       auto vt_chunk = [&](int t, int c) { return t * VCH + (c ^ ((t & (VCH / 2 - 1)) << 1)); };
-      u32x4* vt = sm.t.vtile[wave];
+      u32x4* vt = DMA ? dvs : sm.t.vtile[wave];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
+      for (int rr = 0; rr < (DMA ? 0 : 4); ++rr) {
         const int t = 4 * q4 + rr;  // this lane holds d = lo16 * D/16 ... of row t
         uint32_t w16[D / 32];       // those D/16 elements as 16-bit pairs
         if constexpr (KV == kFP8) {
@@ -1138,6 +1231,7 @@ decode_mfma_kernel(Params p) {
       // lanes a resource does not serve (chunks and arrays are multiples of 8
       // bytes, so no 8-byte read straddles the end); 8 elements take the first
       // 8, 16 or 32 bytes.
+      int nr_off = 0, nr_avail = 0;  // direct loads of the new rows: lane offset, bytes readable
       if constexpr (AP) {
         // wave-uniform (kept in scalar registers: a resource built from vector
         // registers would need a loop over the distinct values)
@@ -1150,20 +1244,28 @@ decode_mfma_kernel(Params p) {
         // every other wave and chunk issues the same loads over resources of
         // size 0, which read nothing (the same instructions keep the same waits)
         const int avail = owner && c0 == 0 ? bytes : 0;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_k), (short)0, avail, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_v), (short)0, avail, kBufferWord3);
+        if constexpr (DMA) {
+          // the whole rows go straight into this wave's LDS staging, 16 bytes
+          // per lane (lanes past the row read nothing), after the first ring
+          // tile's loads (below): the block ids' wait never waits for them
+          nr_off = lane * 16 < D * es ? row + lane * 16 : bytes;
+          nr_avail = avail;
+        } else {
+          const __amdgpu_buffer_rsrc_t rk =
+              __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_k), (short)0, avail, kBufferWord3);
+          const __amdgpu_buffer_rsrc_t rv =
+              __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.new_v), (short)0, avail, kBufferWord3);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          kx[w] = kv_load8<false>(rk, off_k, 8 * w);
-          vx[w] = kv_load8<false>(rv, off_v, 8 * w);
+          for (int w = 0; w < 4; ++w) {
+            kx[w] = kv_load8<false>(rk, off_k, 8 * w);
+            vx[w] = kv_load8<false>(rv, off_v, 8 * w);
+          }
         }
       }
 
       // jr: the ring step's tile of the chunk (wave-uniform); jr >= cn past the
       // end, where the loads return zeros without a memory access
-      auto load_tile = [&](Tile& r, int jr) {
+      auto load_tile = [&](Tile& r, int jr, int stage) {
         const int j = min(jr, cn - 1);
         const int tok0 = (t0 + j) * kTileTokens;
         int phys = __builtin_amdgcn_readlane(ids, j);
@@ -1181,6 +1283,21 @@ decode_mfma_kernel(Params p) {
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k_head + off), (short)0, bytes, kBufferWord3);
         const __amdgpu_buffer_rsrc_t vr =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(v_head + off), (short)0, bytes, kBufferWord3);
+        if constexpr (DMA) {
+          typedef __attribute__((address_space(3))) void lds_void;
+          const i32x4 kd = raw_rsrc(k_head + off, bytes);
+          const i32x4 vd = raw_rsrc(v_head + off, bytes);
+          const uint32_t kl = (uint32_t)(uintptr_t)(lds_void*)sm.t.dk[wave][stage];
+          const uint32_t vl = (uint32_t)(uintptr_t)(lds_void*)sm.t.dv[wave][stage];
+          // every LDS read of this stage (the tile two steps back) is done
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            lds_load16<STREAM>(kd, kl + 1024 * j, (j & 1) ? dk_odd : dk_even, 1024 * j);
+            lds_load16<STREAM>(vd, vl + 1024 * j, (j & 1) ? dv_odd : dv_even, 1024 * j);
+          }
+          return;
+        }
 #pragma unroll
         for (int c = 0; c < KCH; ++c) r.k[c] = kv_load16<STREAM>(kr, k_lane, c * 1024);
 #pragma unroll
@@ -1205,26 +1322,41 @@ decode_mfma_kernel(Params p) {
       Tile buf[NBUF];
 #pragma unroll
       for (int b = 0; b < NBUF - 1; ++b) {
-        load_tile(buf[b], b);
+        load_tile(buf[b], b, b);
         // keep the tiles' loads in ring order, so that waiting for the oldest
         // tile never waits for a younger one
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (AP) {
         if (owner && c0 + cn == n_my) last_phys = __builtin_amdgcn_readlane(ids, cn - 1);
-        // the owner stages the new token once its first tile is in flight
-        if (c0 == 0 && owner) stage_new_token();
+        if constexpr (DMA) {
+          // first chunk only: the staging then holds the rows until the owner
+          // converts them at its second tile (or its only one)
+          if (c0 == 0) {
+            typedef __attribute__((address_space(3))) void lds_void;
+            lds_load16<false>(raw_rsrc(p.new_k, nr_avail), (uint32_t)(uintptr_t)(lds_void*)sm.t.nraw[wave][0], nr_off, 0);
+            lds_load16<false>(raw_rsrc(p.new_v, nr_avail), (uint32_t)(uintptr_t)(lds_void*)sm.t.nraw[wave][1], nr_off, 0);
+          }
+        } else {
+          // the owner stages the new token once its first tile is in flight
+          if (c0 == 0 && owner) stage_new_token();
+        }
       }
       for (int i = 0; i < cn; i += NBUF) {
 #pragma unroll
         for (int b = 0; b < NBUF; ++b) {
-          load_tile(buf[(b + NBUF - 1) % NBUF], i + b + NBUF - 1);
+          load_tile(buf[(b + NBUF - 1) % NBUF], i + b + NBUF - 1, (b + NBUF - 1) % NBUF);
           // a ring step past the wave's last tile computes nothing (its
           // loads read nothing); the kernels holding two row tiles measured
           // faster computing it on zeros than branching around it
-          if (RT == 2 || i + b < cn) compute_tile(buf[b], i + b < cn);
+          if (RT == 2 || i + b < cn) compute_tile(buf[b], i + b < cn, b);
         }
       }
+    }
+    if constexpr (DMA) {
+      // the ring's last direct loads (zeros past the wave's tiles) land in
+      // LDS that the merge below reuses
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     if constexpr (AP) {
@@ -1379,28 +1511,38 @@ hipError_t launch(K kernel, int grid, const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool MT, bool AP, int RT, bool ST, bool BAL, bool LPT>
+template <int D, bool MT, bool AP, int RT, bool ST, bool BAL, bool LPT, bool DMA>
 hipError_t dispatch_mfma_types(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
   if (a.kv_dtype == kBF16 && a.q_dtype == kBF16)
-    return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP, RT, ST, BAL, LPT>, grid, p, s);
+    return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP, RT, ST, BAL, LPT, DMA>, grid, p, s);
   if (a.kv_dtype == kF16 && a.q_dtype == kF16)
-    return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP, RT, ST, BAL, LPT>, grid, p, s);
-  if (a.kv_dtype == kFP8 && a.q_dtype == kBF16)
-    return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP, RT, ST, BAL, LPT>, grid, p, s);
-  if (a.kv_dtype == kFP8 && a.q_dtype == kF16)
-    return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP, RT, ST, BAL, LPT>, grid, p, s);
+    return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP, RT, ST, BAL, LPT, DMA>, grid, p, s);
+  if constexpr (!DMA) {
+    if (a.kv_dtype == kFP8 && a.q_dtype == kBF16)
+      return launch(decode_mfma_kernel<kFP8, kBF16, D, MT, AP, RT, ST, BAL, LPT, false>, grid, p, s);
+    if (a.kv_dtype == kFP8 && a.q_dtype == kF16)
+      return launch(decode_mfma_kernel<kFP8, kF16, D, MT, AP, RT, ST, BAL, LPT, false>, grid, p, s);
+  }
   return hipErrorInvalidValue;
 }
 
 // Kernels with balanced ranges have no order to choose; the others are built
 // with and without the longest-first ranking, so that a launch that does not
-// rank runs no trace of it.
+// rank runs no trace of it.  The LDS ring is built for the one-row-tile
+// kernels over 16-bit caches with 256-byte rows, and taken when the host asks
+// for it.
 template <int D, bool MT, bool AP, int RT, bool ST, bool BAL = false>
 hipError_t dispatch_mfma(const DecodeLaunch& a, int grid, const Params& p, hipStream_t s) {
-  if constexpr (!BAL) {
-    if (p.lpt_shift >= 0) return dispatch_mfma_types<D, MT, AP, RT, ST, false, true>(a, grid, p, s);
+  if constexpr (D == 128 && RT == 1 && !BAL) {
+    if (a.lds_ring && a.kv_dtype != kFP8) {
+      if (p.lpt_shift >= 0) return dispatch_mfma_types<D, MT, AP, RT, ST, false, true, true>(a, grid, p, s);
+      return dispatch_mfma_types<D, MT, AP, RT, ST, false, false, true>(a, grid, p, s);
+    }
   }
-  return dispatch_mfma_types<D, MT, AP, RT, ST, BAL, false>(a, grid, p, s);
+  if constexpr (!BAL) {
+    if (p.lpt_shift >= 0) return dispatch_mfma_types<D, MT, AP, RT, ST, false, true, false>(a, grid, p, s);
+  }
+  return dispatch_mfma_types<D, MT, AP, RT, ST, BAL, false, false>(a, grid, p, s);
 }
 
 template <int D>

@@ -72,6 +72,10 @@ struct DecodeLaunch {
   // call's units; a fixed capacity (the library's own workspace) keeps the
   // partial states of every call clear of the counters of any other.
   int counter_slots = 0;
+  // K/V tiles straight into an LDS ring (one-row-tile kernels over 16-bit
+  // caches with head_dim 128, one workgroup per (sequence, KV head, split)):
+  // chosen for grids that run in several rounds anyway.
+  bool lds_ring = false;
 };
 
 // 16-row tiles of (query token, query head) rows per (sequence, KV head).
