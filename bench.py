@@ -60,21 +60,21 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-step", 1): 161772134,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825", 1): 161355776,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-multi4", 1): 168400896,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-b32-step", 1): 161733222,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-b32", 1): 161316864,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa70b-bf16-47x825-b32-multi4", 1): 168361984,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa8b-bf16-256xU4096-step", 1): 2132192461,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa8b-bf16-256xU4096", 1): 2130027008,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "gqa8b-bf16-256xU4096-multi4", 1): 2148944794,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "mha-f16-64x4096-step", 1): 4299453850,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "mha-f16-64x4096", 1): 4297264435,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "mha-f16-64x4096-multi4", 1): 4301997158,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "fp8-prefix-32xU32768-step", 2): 1305303347,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "fp8-prefix-32xU32768", 2): 1304438067,
-    ("9ec84807338cf6636e72cff23134b8c0bb889798b3b263b59d89421381189604", "fp8-prefix-32xU32768-multi4", 2): 1325145088,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-step", 1): 161760256,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825", 1): 161376256,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-multi4", 1): 168389632,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-b32-step", 1): 161721344,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-b32", 1): 161337344,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-b32-multi4", 1): 168350822,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa8b-bf16-256xU4096-step", 1): 2132146688,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa8b-bf16-256xU4096", 1): 2130046464,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa8b-bf16-256xU4096-multi4", 1): 2148946944,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "mha-f16-64x4096-step", 1): 4299397325,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "mha-f16-64x4096", 1): 4297257984,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "mha-f16-64x4096-multi4", 1): 4301990195,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "fp8-prefix-32xU32768-step", 2): 1305397146,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "fp8-prefix-32xU32768", 2): 1306002534,
+    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "fp8-prefix-32xU32768-multi4", 2): 1326878106,
 }
 
 
@@ -503,6 +503,7 @@ def main():
                      "isolated_launches": len(launch_ms),
                      "measured_stream_peaks": None,  # filled in last (below)
                      "algorithmic_bytes_per_launch": per_call,
+                     "kernel_source_sha256": kernel_source_sha256(),
                      "decode_only_mean_launch_us": round(decode_only_ms * 1e3, 3)},
     }
     # copy-on-write block copy: disjoint (src, dst) block pairs of one layer pool
