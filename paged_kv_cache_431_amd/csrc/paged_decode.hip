@@ -952,11 +952,26 @@ decode_mfma_kernel(Params p) {
       l_run[k] = 0.f;
     }
 
-    // This wave's tiles: a contiguous slice [wb, wb + n_my) of the range.
+    // This wave's tiles: wb, wb + ws, ..., n_my of them.  With one workgroup
+    // per pair and split, a contiguous slice of the range (ws = 1).  With
+    // balanced ranges every 4th tile from t_begin + wave (ws = 4): the 4 waves
+    // walk an item together, front to back, so a shared prefix at the start
+    // of a pair is read in a quarter of the time, and the sequences sharing
+    // it (whose workgroups start it together on one XCD) stay close enough
+    // to find each other's lines in L2 (32K FP8 batch, 8 sequences per
+    // prefix: fetch 1.049 -> 1.017 x the unique K/V bytes, decode 216 -> 211
+    // us).  One workgroup per pair measured no faster this way.
     const int span = it.t_end - it.t_begin;
-    const int per_w = span > 0 ? (span + kDecodeWaves - 1) / kDecodeWaves : 0;
-    const int wb = it.t_begin + wave * per_w;
-    const int n_my = max(0, min(it.t_end, wb + per_w) - wb);
+    constexpr int ws = BAL ? kDecodeWaves : 1;
+    int wb, n_my;
+    if constexpr (ws == 1) {
+      const int per_w = span > 0 ? (span + kDecodeWaves - 1) / kDecodeWaves : 0;
+      wb = it.t_begin + wave * per_w;
+      n_my = max(0, min(it.t_end, wb + per_w) - wb);
+    } else {
+      wb = it.t_begin + wave;
+      n_my = span > wave ? (span - wave + ws - 1) / ws : 0;
+    }
 
     const int32_t* bt_row = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
     const size_t head_bytes = (size_t)p.block_size * ROW;
@@ -980,10 +995,9 @@ decode_mfma_kernel(Params p) {
     // that tile with the new rows (staged in LDS at the start) in place of the
     // loaded ones, and writes them to the pool after its last tile.  No other
     // wave or workgroup reads that position, so nothing waits for the write.
-    const bool owner =
-        AP && it.append && it.t_end == it.n_tiles && wb <= it.n_tiles - 1 && it.n_tiles - 1 < wb + n_my;
+    const bool owner = AP && it.append && it.t_end == it.n_tiles && n_my > 0 && wb + ws * (n_my - 1) == it.n_tiles - 1;
     const int last_tok0 = (it.n_tiles - 1) * kTileTokens;
-    const int stage_tok0 = min(wb + 1, it.n_tiles - 1) * kTileTokens;  // direct loads: where the owner stages
+    const int stage_tok0 = (n_my >= 2 ? wb + ws : wb) * kTileTokens;  // direct loads: where the owner stages
     int last_phys = -1;  // physical block of the last position (owner wave)
 
     auto compute_tile = [&](Tile& r, bool valid, int stage) {
@@ -1087,9 +1101,9 @@ decode_mfma_kernel(Params p) {
         uint32_t w16[D / 32];       // those D/16 elements as 16-bit pairs
         if constexpr (KV == kFP8) {
 #pragma unroll
-          for (int w = 0; w < VDW; ++w) {
-            w16[2 * w] = fp8x2_to_pair<CT, false>(r.v[rr][w]);
-            w16[2 * w + 1] = fp8x2_to_pair<CT, true>(r.v[rr][w]);
+          for (int w = 0; w < VDW; ++w) {  // FP8 V as f16 (exact), the PV product's type
+            w16[2 * w] = fp8x2_to_pair<kF16, false>(r.v[rr][w]);
+            w16[2 * w + 1] = fp8x2_to_pair<kF16, true>(r.v[rr][w]);
           }
         } else {
 #pragma unroll
@@ -1156,7 +1170,17 @@ decode_mfma_kernel(Params p) {
         for (int rr = 0; rr < 4; ++rr) pr[rr] = fast_exp2(s[rr] - m_use);
         l_run[k] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
-        if constexpr (CT == kBF16) {
+        if constexpr (KV == kFP8) {
+          // FP8 V carries 4 significant bits; P rounded once to f16 (11 bits,
+          // round to nearest even) costs about 2e-4 rel-L2 of the output
+          // against the float64 oracle, and one f16 MFMA per 16 rows of d
+          // replaces the hi + lo contraction (fewer VALU and MFMA cycles: the
+          // FP8 4-token step 245 -> 235 us, decode 212 -> 210 us)
+          typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+          const h2v p01 = {(_Float16)pr[0], (_Float16)pr[1]}, p23 = {(_Float16)pr[2], (_Float16)pr[3]};
+          p_hi[k] = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+          p_lo[k] = u32x2{0u, 0u};
+        } else if constexpr (CT == kBF16) {
           float lo_part[4];
           uint32_t hb[4];
 #pragma unroll
@@ -1183,7 +1207,8 @@ decode_mfma_kernel(Params p) {
       //    and once with the lo part of P: the 8 contraction slots of lane
       //    group q4 are (tokens 4 q4 .. 4 q4 + 3, hi) then (the same tokens,
       //    lo), so its A operand is the 8-byte V^T cell of those 4 tokens
-      //    twice and its B operand the hi cell followed by the lo cell
+      //    twice and its B operand the hi cell followed by the lo cell (FP8
+      //    caches: one 16x16x16 f16 MFMA, the cell and the f16 P cell)
       // A operands by transposing reads: lane (4k + m) of each 16-lane group
       // points at 4 elements d = 16n + 4m .. +3 of token 4*q4 + k, and lane j
       // receives element j of those 4 tokens' rows, i.e. V^T[16n + j][4*q4 .. +3]
@@ -1204,8 +1229,15 @@ decode_mfma_kernel(Params p) {
       for (int k = 0; k < RT; ++k) {
         const u32x4 pb = u32x4{p_hi[k][0], p_hi[k][1], p_lo[k][0], p_lo[k][1]};
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-          acc[k][n] = mfma_16x16x32<CT>(u32x4{cell[n][0], cell[n][1], cell[n][0], cell[n][1]}, pb, acc[k][n]);
+        for (int n = 0; n < NT; ++n) {
+          if constexpr (KV == kFP8) {  // f16 V^T cell x f16 P, contraction over the 4 tokens
+            typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+            acc[k][n] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4v, cell[n]),
+                                                              __builtin_bit_cast(h4v, p_hi[k]), acc[k][n], 0, 0, 0);
+          } else {
+            acc[k][n] = mfma_16x16x32<CT>(u32x4{cell[n][0], cell[n][1], cell[n][0], cell[n][1]}, pb, acc[k][n]);
+          }
+        }
       }
       mfma_guard();
       compiler_fence();
@@ -1213,10 +1245,10 @@ decode_mfma_kernel(Params p) {
 
     for (int c0 = 0; c0 < n_my; c0 += 64) {
       const int cn = min(64, n_my - c0);  // tiles in this chunk (>= 1)
-      const int t0 = wb + c0;             // its first tile
+      const int t0 = wb + ws * c0;        // its first tile
       // Lane j holds the physical block of tile t0 + j (clamped into the chunk,
       // so only table entries of blocks the context covers are read).
-      const int ids = bt_row[(t0 + min(lane, cn - 1)) >> p.tile_shift];
+      const int ids = bt_row[(t0 + ws * min(lane, cn - 1)) >> p.tile_shift];
       // Decode step: every wave loads its (sequence, KV head)'s new K and V rows
       // right after the chunk's block ids, so waiting for the ids (L2-resident)
       // never waits for these (cold) rows, and before the chunk's first tile,
@@ -1267,14 +1299,14 @@ decode_mfma_kernel(Params p) {
       // end, where the loads return zeros without a memory access
       auto load_tile = [&](Tile& r, int jr, int stage) {
         const int j = min(jr, cn - 1);
-        const int tok0 = (t0 + j) * kTileTokens;
+        const int tok0 = (t0 + ws * j) * kTileTokens;
         int phys = __builtin_amdgcn_readlane(ids, j);
         const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
         phys = ok ? phys : 0;
         const int rem = it.ctx - tok0;
         r.lim = ok ? (rem < kTileTokens ? rem : kTileTokens) : 0;
         r.tok0 = tok0;
-        const int sub = (t0 + j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
+        const int sub = (t0 + ws * j) & ((1 << p.tile_shift) - 1);  // 16-token tile within the block
         const size_t off = (size_t)phys * block_bytes + (size_t)sub * (kTileTokens * ROW);
         // the rows inside the context only: the unused tail slots of a
         // sequence's last block come back as zeros without being read
