@@ -60,21 +60,21 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-step", 1): 161760256,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825", 1): 161376256,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-multi4", 1): 168389632,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-b32-step", 1): 161721344,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-b32", 1): 161337344,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa70b-bf16-47x825-b32-multi4", 1): 168350822,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa8b-bf16-256xU4096-step", 1): 2132146688,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa8b-bf16-256xU4096", 1): 2130046464,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "gqa8b-bf16-256xU4096-multi4", 1): 2148946944,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "mha-f16-64x4096-step", 1): 4299397325,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "mha-f16-64x4096", 1): 4297257984,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "mha-f16-64x4096-multi4", 1): 4301990195,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "fp8-prefix-32xU32768-step", 2): 1305397146,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "fp8-prefix-32xU32768", 2): 1306002534,
-    ("44d541eea1f44442739ec41fc55e6b0bee6b714f5392947ea07e6ecc3841d8b8", "fp8-prefix-32xU32768-multi4", 2): 1326878106,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-step", 1): 161772608,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825", 1): 161372165,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-multi4", 1): 168386570,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-b32-step", 1): 161733693,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-b32", 1): 161333248,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-b32-multi4", 1): 168347720,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa8b-bf16-256xU4096-step", 1): 2132162496,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa8b-bf16-256xU4096", 1): 2130046403,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa8b-bf16-256xU4096-multi4", 1): 2148936234,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "mha-f16-64x4096-step", 1): 4299390280,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "mha-f16-64x4096", 1): 4297266191,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "mha-f16-64x4096-multi4", 1): 4302002438,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "fp8-prefix-32xU32768-step", 2): 1265857656,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "fp8-prefix-32xU32768", 2): 1266350105,
+    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "fp8-prefix-32xU32768-multi4", 2): 1290751989,
 }
 
 
