@@ -27,9 +27,20 @@ def test_graph_replays_match_eager(types):
     contexts = (1, 17, 300, 825, 0, 2000)
     wl = workloads.Workload("graph-" + types[1], len(contexts), 16, 2, 128, 16, *types, 81, contexts=contexts,
                             extra_blocks=40)
-    layers = 3
-    splits = 3
-    m = 4
+    check_graph(wl, splits=3, m=4)
+
+
+def test_graph_replays_with_the_lds_ring():
+    """100 sequences x 8 KV heads: 800 workgroups, so the decode step and the
+    several-token call (2 query heads x 4 tokens: one row tile) load K/V
+    through the LDS ring inside the captured graph."""
+    contexts = tuple((1, 17, 300, 825, 0, 2000)[i % 6] for i in range(100))
+    wl = workloads.Workload("graph-ring", len(contexts), 16, 8, 128, 16, "bf16", "bf16", "bf16", 83,
+                            contexts=contexts, extra_blocks=40)
+    check_graph(wl, splits=1, m=4, layers=2)
+
+
+def check_graph(wl, splits, m, layers=3):
     cases = _layer_cases(wl, layers)
     plan = cases[0].plan
     stream = torch.cuda.Stream()

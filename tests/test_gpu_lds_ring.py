@@ -65,7 +65,7 @@ def check_step(wl, num_splits=0):
     assert_close(out, one.oracle_decode(), wl.kv_dtype, label=f"{wl.name} step all rows")
 
 
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [16, 32, 64])
 @pytest.mark.parametrize("types", TYPES, ids=lambda t: "-".join(t))
 def test_decode_through_the_lds_ring(types, bs):
     wl = ring_case(types, bs)
