@@ -332,42 +332,44 @@ __device__ __forceinline__ float load_agent(const float* p) {
 // Wait until every store this wave issued has completed.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Store DW = D/16 consecutive outputs (times `mul`) of one output row.
+// Store the DW = D/16 outputs (times `mul`) a thread holds of one output
+// row: a[4 h + q] is element 64 h + 4 chunk + q, so that the 16 threads of a
+// row store 64 contiguous elements per instruction (and read their states
+// from LDS the same way, without bank conflicts).
 template <int D>
 __device__ __forceinline__ void store_out(const Params& p, size_t row, int chunk, const float* a, float mul) {
   constexpr int DW = D / 16;
-  const size_t off = row * D + (size_t)chunk * DW;
+  const size_t off = row * D + (size_t)chunk * 4;
   if (p.out_dtype == kF32) {
     float* o = static_cast<float*>(p.out) + off;
 #pragma unroll
-    for (int e = 0; e < DW; e += 4) {
-      float4 v = make_float4(a[e] * mul, a[e + 1] * mul, a[e + 2] * mul, a[e + 3] * mul);
-      *reinterpret_cast<float4*>(o + e) = v;
+    for (int h = 0; h < DW / 4; ++h) {
+      const float* x = a + 4 * h;
+      *reinterpret_cast<float4*>(o + 64 * h) = make_float4(x[0] * mul, x[1] * mul, x[2] * mul, x[3] * mul);
     }
   } else {
     uint16_t* o = static_cast<uint16_t*>(p.out) + off;
-    uint32_t packed[DW / 2];
 #pragma unroll
-    for (int e = 0; e < DW; e += 2) {
-      // A 16-bit output is the fp32 output rounded to nearest-even: the
-      // products stay rounded fp32 values (the compiler would otherwise fuse
-      // the multiply into a mixed-precision instruction that rounds once).
-      float y0 = a[e] * mul, y1 = a[e + 1] * mul;
-      asm volatile("" : "+v"(y0), "+v"(y1));
-      uint32_t lo, hi;
-      if (p.out_dtype == kBF16) {
-        lo = f32_to_bf16_rne(y0);
-        hi = f32_to_bf16_rne(y1);
-      } else {
-        lo = f32_to_f16_bits(y0);
-        hi = f32_to_f16_bits(y1);
+    for (int h = 0; h < DW / 4; ++h) {
+      uint32_t packed[2];
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        // A 16-bit output is the fp32 output rounded to nearest-even: the
+        // products stay rounded fp32 values (the compiler would otherwise fuse
+        // the multiply into a mixed-precision instruction that rounds once).
+        float y0 = a[4 * h + e] * mul, y1 = a[4 * h + e + 1] * mul;
+        asm volatile("" : "+v"(y0), "+v"(y1));
+        uint32_t lo, hi;
+        if (p.out_dtype == kBF16) {
+          lo = f32_to_bf16_rne(y0);
+          hi = f32_to_bf16_rne(y1);
+        } else {
+          lo = f32_to_f16_bits(y0);
+          hi = f32_to_f16_bits(y1);
+        }
+        packed[e / 2] = lo | (hi << 16);
       }
-      packed[e / 2] = lo | (hi << 16);
-    }
-    if constexpr (DW == 8) {
-      *reinterpret_cast<u32x4*>(o) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-    } else {
-      *reinterpret_cast<u32x2*>(o) = u32x2{packed[0], packed[1]};
+      *reinterpret_cast<u32x2*>(o + 64 * h) = u32x2{packed[0], packed[1]};
     }
   }
 }
@@ -438,13 +440,12 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
   const int cidx = it.unit * RT + k;
   size_t row;
   const bool row_ok = out_row<MT>(p, it, k, g, row);
-  // This thread's elements of the row: chunk * DW + e with one range (16-byte
-  // output stores), chunk + 16 e for partial states, so that every store and
-  // load instruction of the merge covers 64 contiguous bytes of a row
+  // This thread's elements of the row: with one range 64 h + 4 chunk + q
+  // (16-byte LDS reads and output stores, the 16 threads of a row on
+  // consecutive bytes), for partial states chunk + 16 e, so that every store
+  // and load instruction of the merge covers 64 contiguous bytes of a row
   // instead of scattering 4-byte accesses 32 bytes apart.
   const bool whole = it.n_splits_seq == 1;
-  const int e0 = whole ? chunk * DW : chunk;
-  const int es = whole ? 1 : 16;
   float a[DW];
   float mstar = kNegInf, lstar = 0.f;
 #pragma unroll
@@ -456,8 +457,17 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
     for (int w = 0; w < kDecodeWaves; ++w) {
       const float f = mstar == kNegInf ? 0.f : fast_exp2(sm.m[w][g] - mstar);
       lstar += f * sm.l[w][g];
+      if (whole) {
 #pragma unroll
-      for (int e = 0; e < DW; ++e) a[e] += f * sm.acc[w][g][e0 + es * e];
+        for (int h = 0; h < DW / 4; ++h) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.acc[w][g][64 * h + 4 * chunk]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a[4 * h + q] += f * v[q];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < DW; ++e) a[e] += f * sm.acc[w][g][chunk + 16 * e];
+      }
     }
   }
   // a row that sees no position (only with several query tokens, when a
