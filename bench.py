@@ -60,21 +60,21 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-step", 1): 161772608,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825", 1): 161372165,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-multi4", 1): 168386570,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-b32-step", 1): 161733693,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-b32", 1): 161333248,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa70b-bf16-47x825-b32-multi4", 1): 168347720,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa8b-bf16-256xU4096-step", 1): 2132162496,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa8b-bf16-256xU4096", 1): 2130046403,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "gqa8b-bf16-256xU4096-multi4", 1): 2148936234,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "mha-f16-64x4096-step", 1): 4299390280,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "mha-f16-64x4096", 1): 4297266191,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "mha-f16-64x4096-multi4", 1): 4302002438,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "fp8-prefix-32xU32768-step", 2): 1265857656,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "fp8-prefix-32xU32768", 2): 1266350105,
-    ("fcd1bd3c7c0c272cda0d3f3c1ffe78c980531be212b23aff2e52d0d555fa01ca", "fp8-prefix-32xU32768-multi4", 2): 1290751989,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-step", 1): 161769537,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825", 1): 161364992,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-multi4", 1): 168376320,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-b32-step", 1): 161730623,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-b32", 1): 161326080,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-b32-multi4", 1): 168337408,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa8b-bf16-256xU4096-step", 1): 2132162609,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa8b-bf16-256xU4096", 1): 2130022403,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa8b-bf16-256xU4096-multi4", 1): 2148937735,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "mha-f16-64x4096-step", 1): 4299398407,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "mha-f16-64x4096", 1): 4297251840,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "mha-f16-64x4096-multi4", 1): 4301986816,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "fp8-prefix-32xU32768-step", 2): 1266103132,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "fp8-prefix-32xU32768", 2): 1266300718,
+    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "fp8-prefix-32xU32768-multi4", 2): 1290022412,
 }
 
 
