@@ -116,9 +116,10 @@ def test_empty_query_table_is_a_no_op():
     assert out.shape[0] == 0
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
-def test_16bit_output_is_the_rounded_fp32_output(out_dtype):
-    wl = small(16, 2, 128, 16, "bf16", "bf16", "bf16", seed=33)
+def test_16bit_output_is_the_rounded_fp32_output(out_dtype, d):
+    wl = small(16, 2, d, 16, "bf16", "bf16", "bf16", seed=33)
     c = prepared(wl)
     q, qs = workloads.multi_queries(wl, NEW, device="cuda")
     o32 = c.multi(q, qs, max(NEW))

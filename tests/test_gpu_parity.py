@@ -133,9 +133,15 @@ def test_repeat_calls_are_bitwise_identical_and_workspace_is_reusable():
     assert_close(outs[0], c.oracle_decode(), "bf16", label="repeat")
 
 
+@pytest.mark.parametrize("d,kv", [(128, "bf16"), (64, "bf16"), (128, "f32"), (64, "f32")],
+                         ids=["d128-mfma", "d64-mfma", "d128-vector", "d64-vector"])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
-def test_16bit_output_is_the_rounded_fp32_output(out_dtype):
-    wl = small(16, 2, 128, 16, "bf16", "bf16", "bf16", seed=17)
+def test_16bit_output_is_the_rounded_fp32_output(out_dtype, d, kv):
+    """Each thread of the merge stores its elements of a row in 16-byte
+    groups (two per row of 128, one per row of 64): every element of the
+    16-bit output is the fp32 output rounded to nearest-even, on both paths."""
+    q = "f32" if kv == "f32" else "bf16"
+    wl = small(16, 2, d, 16, q, kv, kv, seed=17)
     c = Case(wl)
     c.scatter()
     f32 = c.decode()
