@@ -22,6 +22,10 @@
 //   When the grid does not fit on the GPU at once, workgroups take the
 //   sequences longest first (each workgroup ranks all context lengths in
 //   LDS), so the workgroups that start last hold the shortest work.
+//   Balanced ranges (few pairs with long contexts): every workgroup takes an
+//   equal contiguous range of all pairs' tiles instead, laid out KV head by
+//   KV head with one head block per XCD; a pair cut between ranges merges
+//   through the workspace like splits.
 //
 // Memory pipeline (the kernel is bound by HBM bandwidth: each K/V byte is
 // used by G query rows only)
@@ -37,6 +41,10 @@
 //   workgroup is the only reader of a (sequence, KV head)'s K/V (decode, and
 //   several query tokens held by one row group) the loads are non-temporal:
 //   nothing re-reads them.
+//   LDS ring: over 16-bit caches with 256-byte rows and grids of more than
+//   three workgroups per CU, the tiles come straight into a per-wave ring in
+//   LDS (buffer loads to LDS, waits placed by the kernel) instead of through
+//   registers.
 //
 // Matrix-core path (16-bit or FP8 caches, block_size 16 x 2^k)
 //   Scores: S^T[token][g] = K[token][:] . Q[g][:] with v_mfma_f32_16x16x32
