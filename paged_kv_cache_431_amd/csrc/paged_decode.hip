@@ -382,6 +382,45 @@ __device__ __forceinline__ void store_out(const Params& p, size_t row, int chunk
   }
 }
 
+// Store DW = D/16 consecutive outputs (times `mul`) of one output row,
+// elements chunk * DW + e (the balanced-range kernels' merge).  Rounding as
+// in store_out.
+template <int D>
+__device__ __forceinline__ void store_out_contig(const Params& p, size_t row, int chunk, const float* a, float mul) {
+  constexpr int DW = D / 16;
+  const size_t off = row * D + (size_t)chunk * DW;
+  if (p.out_dtype == kF32) {
+    float* o = static_cast<float*>(p.out) + off;
+#pragma unroll
+    for (int e = 0; e < DW; e += 4) {
+      float4 v = make_float4(a[e] * mul, a[e + 1] * mul, a[e + 2] * mul, a[e + 3] * mul);
+      *reinterpret_cast<float4*>(o + e) = v;
+    }
+  } else {
+    uint16_t* o = static_cast<uint16_t*>(p.out) + off;
+    uint32_t packed[DW / 2];
+#pragma unroll
+    for (int e = 0; e < DW; e += 2) {
+      float y0 = a[e] * mul, y1 = a[e + 1] * mul;
+      asm volatile("" : "+v"(y0), "+v"(y1));
+      uint32_t lo, hi;
+      if (p.out_dtype == kBF16) {
+        lo = f32_to_bf16_rne(y0);
+        hi = f32_to_bf16_rne(y1);
+      } else {
+        lo = f32_to_f16_bits(y0);
+        hi = f32_to_f16_bits(y1);
+      }
+      packed[e / 2] = lo | (hi << 16);
+    }
+    if constexpr (DW == 8) {
+      *reinterpret_cast<u32x4*>(o) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    } else {
+      *reinterpret_cast<u32x2*>(o) = u32x2{packed[0], packed[1]};
+    }
+  }
+}
+
 // Store DW outputs of one output row, elements c + 16 e (times `mul`): the
 // layout the cross-range merge works in, where each store instruction of a
 // row's 16 threads covers contiguous bytes.  Rounding as in store_out.
@@ -439,7 +478,7 @@ __device__ void write_zeros(const Params& p, const Item& it, int k) {
 // partial state and let the last range of the (sequence, KV head, row tile)
 // combine all of them.  Row tile k of a workgroup of RT row tiles has its
 // own counter and partial rows: index unit * RT + k.
-template <int D, bool MT, int RT>
+template <int D, bool MT, int RT, bool QUAD = true>
 __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm) {
   constexpr int DW = D / 16;
   const int t = threadIdx.x;
@@ -452,7 +491,10 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
   // (16-byte LDS reads and output stores, the 16 threads of a row on
   // consecutive bytes), for partial states chunk + 16 e, so that every store
   // and load instruction of the merge covers 64 contiguous bytes of a row
-  // instead of scattering 4-byte accesses 32 bytes apart.
+  // instead of scattering 4-byte accesses 32 bytes apart.  The kernels with
+  // balanced ranges (QUAD false) keep chunk * DW + e for one range: at their
+  // register limit the wider reads made the two-row-tile kernel spill 16
+  // bytes more per lane (bf16 4-token batch of 32 long contexts 435 -> 440 us).
   const bool whole = it.n_splits_seq == 1;
   float a[DW];
   float mstar = kNegInf, lstar = 0.f;
@@ -465,7 +507,7 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
     for (int w = 0; w < kDecodeWaves; ++w) {
       const float f = mstar == kNegInf ? 0.f : fast_exp2(sm.m[w][g] - mstar);
       lstar += f * sm.l[w][g];
-      if (whole) {
+      if (QUAD && whole) {
 #pragma unroll
         for (int h = 0; h < DW / 4; ++h) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.acc[w][g][64 * h + 4 * chunk]);
@@ -473,15 +515,20 @@ __device__ void finish(const Params& p, const Item& it, int k, MergeSmem<D>& sm)
           for (int q = 0; q < 4; ++q) a[4 * h + q] += f * v[q];
         }
       } else {
+        const int e0 = whole ? chunk * DW : chunk;
+        const int es = whole ? 1 : 16;
 #pragma unroll
-        for (int e = 0; e < DW; ++e) a[e] += f * sm.acc[w][g][chunk + 16 * e];
+        for (int e = 0; e < DW; ++e) a[e] += f * sm.acc[w][g][e0 + es * e];
       }
     }
   }
   // a row that sees no position (only with several query tokens, when a
   // sequence has more new tokens than cached ones) gets 0
   if (whole) {
-    if (row_ok) store_out<D>(p, row, chunk, a, lstar > 0.f ? p.v_scale / lstar : 0.f);
+    if (row_ok) {
+      if constexpr (QUAD) store_out<D>(p, row, chunk, a, lstar > 0.f ? p.v_scale / lstar : 0.f);
+      else store_out_contig<D>(p, row, chunk, a, lstar > 0.f ? p.v_scale / lstar : 0.f);
+    }
     return;
   }
   const size_t base = (size_t)cidx * p.num_splits * R + g;  // partial row of split 0
@@ -1441,7 +1488,7 @@ decode_mfma_kernel(Params p) {
         sm.merge.l[wave][lo16] = l_row;
       }
       __syncthreads();
-      finish<D, MT, RT>(p, it, k, sm.merge);
+      finish<D, MT, RT, !BAL>(p, it, k, sm.merge);
     }
   };
 
