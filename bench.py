@@ -60,21 +60,21 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-step", 1): 161769537,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825", 1): 161364992,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-multi4", 1): 168376320,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-b32-step", 1): 161730623,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-b32", 1): 161326080,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa70b-bf16-47x825-b32-multi4", 1): 168337408,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa8b-bf16-256xU4096-step", 1): 2132162609,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa8b-bf16-256xU4096", 1): 2130022403,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "gqa8b-bf16-256xU4096-multi4", 1): 2148937735,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "mha-f16-64x4096-step", 1): 4299398407,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "mha-f16-64x4096", 1): 4297251840,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "mha-f16-64x4096-multi4", 1): 4301986816,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "fp8-prefix-32xU32768-step", 2): 1266103132,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "fp8-prefix-32xU32768", 2): 1266300718,
-    ("f7a7e2e305c997888abf0976a880583a13bd1203f9f60e7347ddc4e1e1942e62", "fp8-prefix-32xU32768-multi4", 2): 1290022412,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-step", 1): 161763396,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825", 1): 161364992,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-multi4", 1): 168395776,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-b32-step", 1): 161724481,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-b32", 1): 161326080,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-b32-multi4", 1): 168356864,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa8b-bf16-256xU4096-step", 1): 2132156280,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa8b-bf16-256xU4096", 1): 2130032641,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa8b-bf16-256xU4096-multi4", 1): 2148934673,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "mha-f16-64x4096-step", 1): 4299397935,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "mha-f16-64x4096", 1): 4297243648,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "mha-f16-64x4096-multi4", 1): 4301991938,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "fp8-prefix-32xU32768-step", 2): 1265847854,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "fp8-prefix-32xU32768", 2): 1266192491,
+    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "fp8-prefix-32xU32768-multi4", 2): 1290196569,
 }
 
 
