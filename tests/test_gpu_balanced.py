@@ -12,7 +12,8 @@ workgroup) against the float64 oracle, through the C ABI:
   * contexts longer than max_context_len are attended over in full;
   * several new query tokens per sequence whose rows of a pair fit one
     workgroup take balanced ranges too (one and two row tiles, ragged
-    token counts including none).
+    token counts including none);
+  * 16-bit outputs are the fp32 outputs rounded, from both merges.
 """
 
 import numpy as np
@@ -145,3 +146,24 @@ def test_balanced_ranges_with_several_query_tokens(kv, h_q, ms):
     forced = c.multi(q, qs, max_m, num_splits=3)
     torch.cuda.synchronize()
     assert_close(forced, ref, wl.kv_dtype, label=f"{wl.name}-splits3")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_balanced_ranges_16bit_output_is_the_rounded_fp32_output(out_dtype):
+    """Short sequences that fit inside one range write their rows from the
+    workgroup's own merge (consecutive elements per thread), long ones from
+    the cross-range merge (every 16th element): both round the fp32 output
+    to nearest-even, for decode and for several query tokens."""
+    wl = _wl("balanced-out16", MIXED, kv="bf16", seed=103)
+    c = Case(wl)
+    c.scatter()
+    f32 = c.decode()
+    o16 = c.decode(out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, f32.to(out_dtype))
+    ms = (1, 4, 2, 3, 0, 4, 1, 2, 4, 3)
+    q, qs = workloads.multi_queries(wl, ms, device="cuda")
+    m32 = c.multi(q, qs, max(ms))
+    m16 = c.multi(q, qs, max(ms), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(m16, m32.to(out_dtype))
