@@ -104,6 +104,7 @@
 #include "kv_chunk.h"
 #include "pkv_internal.h"
 
+
 namespace pkv {
 namespace {
 
@@ -134,6 +135,7 @@ struct Params {
   const int32_t* query_start;
   int num_query_tokens, max_query_len;
   int lpt_shift;   // decode: >= 0 takes sequences longest first (tile counts >> lpt_shift), -1 in order
+  int pace_lo, pace_hi;  // workgroups [pace_lo, pace_hi) pace their tiles (a CU each); empty: none
   int balanced;    // decode: tiles of all (sequence, KV head) pairs cut into gridDim.x equal ranges
   int row_tiles;   // 16-row tiles of (query token, head) rows per (sequence, KV head)
   int row_groups;  // workgroups per (sequence, KV head, split): row_tiles / RT, rounded up
@@ -799,6 +801,12 @@ __device__ __forceinline__ uint32_t kv_load4(__amdgpu_buffer_rsrc_t r, int lane_
   return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, off, STREAM ? 2 : 0);
 }
 
+// Pacing of a workgroup alone on its CU: after each tile it waits this many
+// quarters of the tile's step time (5: a quarter more than the step took),
+// when the workgroup holds at least kPaceMinTiles tiles (8 per wave).
+constexpr int kPaceShare4 = 5;
+constexpr int kPaceMinTiles = 8 * kDecodeWaves;
+
 // One 16-byte-per-lane buffer load straight into LDS: lane l's 16 bytes land
 // at LDS byte address lds + 16 l; bytes past the resource's size arrive as
 // zeros.  Written as assembly, so that the compiler, which does not model
@@ -858,7 +866,7 @@ struct MfmaTile {
 // DMA: K/V tiles (16-bit, 256-byte rows, one row tile) come straight into an
 // LDS ring instead of through registers; its 64 KiB per workgroup leave room
 // for two workgroups per CU.
-template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM, bool BAL, bool LPT, bool DMA>
+template <int KV, int CT, int D, bool MT, bool AP, int RT, bool STREAM, bool BAL, bool LPT, bool DMA, bool PACE = false>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     RT == 1 && !BAL && !DMA ? kDecodeWavesPerSimd : 2))) void
 decode_mfma_kernel(Params p) {
@@ -1439,6 +1447,16 @@ decode_mfma_kernel(Params p) {
           if (c0 == 0 && owner) stage_new_token();
         }
       }
+      // Pacing (PACE, launched only when some CUs hold one workgroup and
+      // others two): a workgroup alone on its CU waits after each tile, in
+      // short sleeps on the real-time counter (100 MHz), for a share of the
+      // time the tile's step took (from the second step on: the first
+      // includes the start's dependent reads).  Wave-uniform; its loads of
+      // the next tiles are in flight meanwhile.
+      static_assert(!PACE || (!DMA && !BAL && !MT && RT == 1 && NBUF == 2), "pacing: the one-row-tile register ring");
+      const bool pace = PACE && (int)blockIdx.x >= p.pace_lo && (int)blockIdx.x < p.pace_hi &&
+                        it.t_end - it.t_begin >= kPaceMinTiles;
+      uint64_t t_step = 0;
       for (int i = 0; i < cn; i += NBUF) {
 #pragma unroll
         for (int b = 0; b < NBUF; ++b) {
@@ -1447,6 +1465,20 @@ decode_mfma_kernel(Params p) {
           // loads read nothing); the kernels holding two row tiles measured
           // faster computing it on zeros than branching around it
           if (RT == 2 || i + b < cn) compute_tile(buf[b], i + b < cn, b);
+          if (PACE && __builtin_expect(pace, 0)) {
+            const uint64_t now = __builtin_amdgcn_s_memrealtime();
+            if (t_step != 0 && i + b < cn) {
+              const uint64_t until = now + (now - t_step) * kPaceShare4 / 4;
+              uint64_t t = now;
+              while (t < until) {
+                __builtin_amdgcn_s_sleep(2);
+                t = __builtin_amdgcn_s_memrealtime();
+              }
+              t_step = t;
+            } else {
+              t_step = now;
+            }
+          }
         }
       }
     }
@@ -1639,6 +1671,16 @@ hipError_t dispatch_mfma(const DecodeLaunch& a, int grid, const Params& p, hipSt
   if constexpr (!BAL) {
     if (p.lpt_shift >= 0) return dispatch_mfma_types<D, MT, AP, RT, ST, false, true, false>(a, grid, p, s);
   }
+  if constexpr (D == 128 && RT == 1 && !BAL && !MT) {
+    // pacing of the workgroups alone on their CUs: the one-row-tile register
+    // ring over 16-bit caches (FP8 tiles measured slower paced)
+    if (p.pace_hi > p.pace_lo) {
+      if (a.kv_dtype == kBF16 && a.q_dtype == kBF16)
+        return launch(decode_mfma_kernel<kBF16, kBF16, D, false, AP, 1, ST, false, false, false, true>, grid, p, s);
+      if (a.kv_dtype == kF16 && a.q_dtype == kF16)
+        return launch(decode_mfma_kernel<kF16, kF16, D, false, AP, 1, ST, false, false, false, true>, grid, p, s);
+    }
+  }
   return dispatch_mfma_types<D, MT, AP, RT, ST, BAL, false, false>(a, grid, p, s);
 }
 
@@ -1728,6 +1770,12 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.v_scale_enc = a.v_scale_enc;
   const int grid = p.balanced ? a.balanced_workgroups : ((p.units + 7) / 8) * 8 * p.row_groups * a.num_splits;
   if (grid == 0) return hipSuccess;
+  p.pace_lo = p.pace_hi = 0;
+  if (a.pace && !p.balanced && !multi && grid > kComputeUnits && 2 * grid <= 3 * kComputeUnits &&
+      a.tiles_per_split >= kPaceMinTiles) {
+    p.pace_lo = grid - kComputeUnits;
+    p.pace_hi = kComputeUnits;
+  }
   if (a.head_dim == 128) return dispatch<128>(a, grid, p, stream);
   if (a.head_dim == 64) return dispatch<64>(a, grid, p, stream);
   return hipErrorInvalidValue;

@@ -68,6 +68,13 @@ struct DecodeLaunch {
   // sequences are taken in decreasing order of their tile count shifted
   // right by this many bits (ties in index order).
   int lpt_shift = -1;
+  // Pacing (decode and the step, one workgroup per pair and split): when the
+  // grid holds more workgroups than the GPU has CUs but fewer than twice as
+  // many, the dispatcher puts workgroups 0 .. kComputeUnits - 1 on CUs of
+  // their own and the rest beside the first ones, so workgroups grid -
+  // kComputeUnits .. kComputeUnits - 1 have a CU to themselves.  Those
+  // pace their tiles, leaving HBM to the CUs that hold two workgroups.
+  bool pace = false;
   // Counters region of the workspace, in int32 slots: 0 sizes it for this
   // call's units; a fixed capacity (the library's own workspace) keeps the
   // partial states of every call clear of the counters of any other.
