@@ -1448,11 +1448,11 @@ decode_mfma_kernel(Params p) {
         }
       }
       // Pacing (PACE, launched only when some CUs hold one workgroup and
-      // others two): a workgroup alone on its CU waits after each tile, in
-      // short sleeps on the real-time counter (100 MHz), for a share of the
-      // time the tile's step took (from the second step on: the first
-      // includes the start's dependent reads).  Wave-uniform; its loads of
-      // the next tiles are in flight meanwhile.
+      // others two): a workgroup alone on its CU waits after each tile but
+      // its last, in short sleeps on the real-time counter (100 MHz), for a
+      // share of the time the tile's step took (from the second step on: the
+      // first includes the start's dependent reads).  Wave-uniform; its loads
+      // of the next tiles are in flight meanwhile.
       static_assert(!PACE || (!DMA && !BAL && !MT && RT == 1 && NBUF == 2), "pacing: the one-row-tile register ring");
       const bool pace = PACE && (int)blockIdx.x >= p.pace_lo && (int)blockIdx.x < p.pace_hi &&
                         it.t_end - it.t_begin >= kPaceMinTiles;
@@ -1467,7 +1467,8 @@ decode_mfma_kernel(Params p) {
           if (RT == 2 || i + b < cn) compute_tile(buf[b], i + b < cn, b);
           if (PACE && __builtin_expect(pace, 0)) {
             const uint64_t now = __builtin_amdgcn_s_memrealtime();
-            if (t_step != 0 && i + b < cn) {
+            // no wait after the wave's last tile: only its merge is left
+            if (t_step != 0 && c0 + i + b + 1 < n_my) {
               const uint64_t until = now + (now - t_step) * kPaceShare4 / 4;
               uint64_t t = now;
               while (t < until) {
