@@ -60,21 +60,21 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-step", 1): 161763396,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825", 1): 161364992,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-multi4", 1): 168395776,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-b32-step", 1): 161724481,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-b32", 1): 161326080,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa70b-bf16-47x825-b32-multi4", 1): 168356864,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa8b-bf16-256xU4096-step", 1): 2132156280,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa8b-bf16-256xU4096", 1): 2130032641,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "gqa8b-bf16-256xU4096-multi4", 1): 2148934673,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "mha-f16-64x4096-step", 1): 4299397935,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "mha-f16-64x4096", 1): 4297243648,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "mha-f16-64x4096-multi4", 1): 4301991938,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "fp8-prefix-32xU32768-step", 2): 1265847854,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "fp8-prefix-32xU32768", 2): 1266192491,
-    ("1233993dee27c3689d4e11bccee65ae33cdd762f6f9e5e23f4cd44296c13fee0", "fp8-prefix-32xU32768-multi4", 2): 1290196569,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-step", 1): 161783871,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825", 1): 161358848,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-multi4", 1): 168376320,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-b32-step", 1): 161744967,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-b32", 1): 161319936,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-b32-multi4", 1): 168337408,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa8b-bf16-256xU4096-step", 1): 2132165439,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa8b-bf16-256xU4096", 1): 2130027520,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa8b-bf16-256xU4096-multi4", 1): 2148932635,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "mha-f16-64x4096-step", 1): 4299381783,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "mha-f16-64x4096", 1): 4297233408,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "mha-f16-64x4096-multi4", 1): 4301995008,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "fp8-prefix-32xU32768-step", 2): 1267016293,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "fp8-prefix-32xU32768", 2): 1268252169,
+    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "fp8-prefix-32xU32768-multi4", 2): 1290844314,
 }
 
 
