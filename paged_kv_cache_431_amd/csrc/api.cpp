@@ -277,7 +277,7 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
                                              : -1;
   a.lds_ring = lds_ring_fits(matrix_core, balanced, kv_dtype, head_dim, multi, row_tiles) &&
                decode_grid(num_seqs, h_kv, row_groups, n) > (int64_t)pkv::kComputeUnits * pkv::kDecodeWavesPerSimd;
-  a.pace = matrix_core && balanced == 0 && !multi;
+  a.pace = matrix_core && balanced == 0;
   const hipError_t e = pkv::launch_decode(a, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

@@ -136,6 +136,7 @@ struct Params {
   int num_query_tokens, max_query_len;
   int lpt_shift;   // decode: >= 0 takes sequences longest first (tile counts >> lpt_shift), -1 in order
   int pace_lo, pace_hi;  // workgroups [pace_lo, pace_hi) pace their tiles (a CU each); empty: none
+  int pace_share32;      // a paced wave waits this many 32nds of each tile's step time
   int balanced;    // decode: tiles of all (sequence, KV head) pairs cut into gridDim.x equal ranges
   int row_tiles;   // 16-row tiles of (query token, head) rows per (sequence, KV head)
   int row_groups;  // workgroups per (sequence, KV head, split): row_tiles / RT, rounded up
@@ -801,11 +802,20 @@ __device__ __forceinline__ uint32_t kv_load4(__amdgpu_buffer_rsrc_t r, int lane_
   return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, off, STREAM ? 2 : 0);
 }
 
-// Pacing of a workgroup alone on its CU: after each tile it waits this many
-// quarters of the tile's step time (5: a quarter more than the step took),
-// when the workgroup holds at least kPaceMinTiles tiles (8 per wave).
-constexpr int kPaceShare4 = 5;
+// Pacing of a workgroup alone on its CU: after each tile it waits
+// Params::pace_share32 / 32 of the tile's step time, when the workgroup holds
+// at least kPaceMinTiles tiles (8 per wave).  The share grows with the number
+// of CUs holding two workgroups (S = grid - kComputeUnits): the lone
+// workgroups should end with the shared CUs, and the more CUs share, the
+// slower each of them reads.  Measured best shares (in eighths, 16-bit
+// caches, 8 KiB tiles) were 8, 9-10, 10-11 and 12 for S = 16-24, 64, 96 and
+// 120-128 with one row tile, and 1.5-2 eighths less with two row tiles (their
+// tiles take longer); past the best share the lone workgroups end last, and
+// the time grows fast, so the line below stays at or under it.
 constexpr int kPaceMinTiles = 8 * kDecodeWaves;
+__host__ __device__ constexpr int pace_share32(int shared_cus, int row_tiles) {
+  return (row_tiles == 2 ? 26 : 32) + (shared_cus > 16 ? (shared_cus - 16) / 7 : 0);
+}
 
 // One 16-byte-per-lane buffer load straight into LDS: lane l's 16 bytes land
 // at LDS byte address lds + 16 l; bytes past the resource's size arrive as
@@ -1453,7 +1463,7 @@ decode_mfma_kernel(Params p) {
       // share of the time the tile's step took (from the second step on: the
       // first includes the start's dependent reads).  Wave-uniform; its loads
       // of the next tiles are in flight meanwhile.
-      static_assert(!PACE || (!DMA && !BAL && !MT && RT == 1 && NBUF == 2), "pacing: the one-row-tile register ring");
+      static_assert(!PACE || (!DMA && !BAL && NBUF == 2), "pacing: the register ring of 8 KiB tiles");
       const bool pace = PACE && (int)blockIdx.x >= p.pace_lo && (int)blockIdx.x < p.pace_hi &&
                         it.t_end - it.t_begin >= kPaceMinTiles;
       uint64_t t_step = 0;
@@ -1469,7 +1479,7 @@ decode_mfma_kernel(Params p) {
             const uint64_t now = __builtin_amdgcn_s_memrealtime();
             // no wait after the wave's last tile: only its merge is left
             if (t_step != 0 && c0 + i + b + 1 < n_my) {
-              const uint64_t until = now + (now - t_step) * kPaceShare4 / 4;
+              const uint64_t until = now + (now - t_step) * (uint64_t)p.pace_share32 / 32;
               uint64_t t = now;
               while (t < until) {
                 __builtin_amdgcn_s_sleep(2);
@@ -1672,14 +1682,16 @@ hipError_t dispatch_mfma(const DecodeLaunch& a, int grid, const Params& p, hipSt
   if constexpr (!BAL) {
     if (p.lpt_shift >= 0) return dispatch_mfma_types<D, MT, AP, RT, ST, false, true, false>(a, grid, p, s);
   }
-  if constexpr (D == 128 && RT == 1 && !BAL && !MT) {
-    // pacing of the workgroups alone on their CUs: the one-row-tile register
-    // ring over 16-bit caches (FP8 tiles measured slower paced)
+  if constexpr (D == 128 && !BAL && ((!MT && RT == 1) || (MT && RT == 2 && ST))) {
+    // pacing of the workgroups alone on their CUs: the register ring over
+    // 16-bit caches (FP8 tiles measured slower paced), for one token per
+    // sequence, and for several whose two row tiles one workgroup holds as
+    // the only reader of its K/V
     if (p.pace_hi > p.pace_lo) {
       if (a.kv_dtype == kBF16 && a.q_dtype == kBF16)
-        return launch(decode_mfma_kernel<kBF16, kBF16, D, false, AP, 1, ST, false, false, false, true>, grid, p, s);
+        return launch(decode_mfma_kernel<kBF16, kBF16, D, MT, AP, RT, ST, false, false, false, true>, grid, p, s);
       if (a.kv_dtype == kF16 && a.q_dtype == kF16)
-        return launch(decode_mfma_kernel<kF16, kF16, D, false, AP, 1, ST, false, false, false, true>, grid, p, s);
+        return launch(decode_mfma_kernel<kF16, kF16, D, MT, AP, RT, ST, false, false, false, true>, grid, p, s);
     }
   }
   return dispatch_mfma_types<D, MT, AP, RT, ST, BAL, false, false>(a, grid, p, s);
@@ -1771,11 +1783,12 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.v_scale_enc = a.v_scale_enc;
   const int grid = p.balanced ? a.balanced_workgroups : ((p.units + 7) / 8) * 8 * p.row_groups * a.num_splits;
   if (grid == 0) return hipSuccess;
-  p.pace_lo = p.pace_hi = 0;
-  if (a.pace && !p.balanced && !multi && grid > kComputeUnits && 2 * grid <= 3 * kComputeUnits &&
+  p.pace_lo = p.pace_hi = p.pace_share32 = 0;
+  if (a.pace && !p.balanced && grid > kComputeUnits && 2 * grid <= 3 * kComputeUnits &&
       a.tiles_per_split >= kPaceMinTiles) {
     p.pace_lo = grid - kComputeUnits;
     p.pace_hi = kComputeUnits;
+    p.pace_share32 = pace_share32(grid - kComputeUnits, multi_tiles_per_workgroup(p.row_tiles));
   }
   if (a.head_dim == 128) return dispatch<128>(a, grid, p, stream);
   if (a.head_dim == 64) return dispatch<64>(a, grid, p, stream);

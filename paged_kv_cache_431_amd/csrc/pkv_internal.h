@@ -68,7 +68,7 @@ struct DecodeLaunch {
   // sequences are taken in decreasing order of their tile count shifted
   // right by this many bits (ties in index order).
   int lpt_shift = -1;
-  // Pacing (decode and the step, one workgroup per pair and split): when the
+  // Pacing (one workgroup per pair, split and row group): when the
   // grid holds more workgroups than the GPU has CUs but fewer than twice as
   // many, the dispatcher puts workgroups 0 .. kComputeUnits - 1 on CUs of
   // their own and the rest beside the first ones, so workgroups grid -

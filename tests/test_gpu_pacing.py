@@ -6,9 +6,11 @@ tiles wait after each tile, which changes when they read and nothing they
 compute.  The cases are 40 sequences x 8 KV heads (320 workgroups, the
 70B-style layer's head shape) with ragged contexts: pairs too short to be
 paced beside paced ones, empty sequences, and lengths that leave the four
-waves of a workgroup unequal tile counts.  Checks:
+waves of a workgroup unequal tile counts.  Decode, the one-launch step and
+several new query tokens (up to 4 tokens of 8 query heads: two row tiles,
+held by one workgroup) are paced.  Checks:
   * every output row against the oracle;
-  * the output bit-equal to the same sequences decoded in a grid below the
+  * the output bit-equal to the same sequences run in a grid below the
     window (the first 30 sequences: 240 workgroups, none paced);
   * the one-launch step bit-equal to scatter + decode, pools included."""
 
@@ -50,6 +52,7 @@ def test_grid_is_inside_the_paced_window():
     wl = paced_case(TYPES[0], 91)
     max_ctx = workloads.plan(wl).max_context_len
     assert pkv.pkv_decode_num_splits(NUM_SEQS, H_Q, H_KV, D, BS, max_ctx, 0) == 1
+    assert pkv.pkv_multi_num_splits(NUM_SEQS, H_Q, H_KV, D, BS, 4, max_ctx, 0) == 1
     assert 256 < NUM_SEQS * H_KV <= 384 and SUBSET * H_KV <= 256
 
 
@@ -91,3 +94,27 @@ def test_paced_step(types):
     assert torch.equal(one.t.k_cache.view(torch.uint8), two.t.k_cache.view(torch.uint8)), f"{wl.name}: K pool"
     assert torch.equal(one.t.v_cache.view(torch.uint8), two.t.v_cache.view(torch.uint8)), f"{wl.name}: V pool"
     assert_close(out, one.oracle_decode(), wl.kv_dtype, label=f"{wl.name} step all rows")
+
+
+@pytest.mark.parametrize("types", TYPES, ids=lambda t: "-".join(t))
+def test_paced_several_query_tokens(types):
+    wl = paced_case(types, 95)
+    ms = [(4, 3, 4, 1, 2)[i % 5] for i in range(NUM_SEQS)]  # ragged; more tokens than cached ones included
+    print(f"[case] {wl.name} new tokens", flush=True)
+    c = Case(wl)
+    c.scatter()
+    q, qs = workloads.multi_queries(wl, ms, device="cuda")
+    out = c.multi(q, qs, max(ms))
+    torch.cuda.synchronize()
+    assert_close(out, c.oracle_multi(q, qs), wl.kv_dtype, label=f"{wl.name} several tokens")
+
+    print(f"[case] {wl.name} new tokens, unpaced subset", flush=True)
+    rows = int(qs[SUBSET])
+    sub = torch.empty((rows, H_Q, D), dtype=torch.float32, device="cuda")
+    pkv.pkv_paged_attention_multi(sub, q[:rows].contiguous(), c.t.k_cache, c.t.v_cache,
+                                  c.block_tables[:SUBSET].contiguous(), c.context_lens[:SUBSET].contiguous(),
+                                  torch.from_numpy(np.ascontiguousarray(qs[:SUBSET + 1])).cuda(),
+                                  max_query_len=max(ms), max_context_len=c.plan.max_context_len,
+                                  k_scale=c.t.k_scale, v_scale=c.t.v_scale, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(sub, out[:rows]), f"{wl.name}: paced rows differ from the unpaced launch"
