@@ -1499,21 +1499,20 @@ decode_mfma_kernel(Params p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
+    // The new token's slot and rows (the owner's lanes of its rows): the rows
+    // leave the LDS, which the merge reuses, for registers, and are stored
+    // after the merge, whose barriers would otherwise wait for the store.
+    [[maybe_unused]] uint8_t* new_dst = nullptr;
+    [[maybe_unused]] Chunk8<KV> new_rows{};
     if constexpr (AP) {
-      // the new token into its slot (its rows are still in LDS)
       if (owner && (unsigned)last_phys < (unsigned)p.num_blocks && lane < 2 * CH) {
         const bool is_v = lane >= CH;
         const int c = is_v ? lane - CH : lane;
         const int pos = it.ctx - 1;
         const int off = pos - (pos / p.block_size) * p.block_size;
         const size_t dst = (((size_t)last_phys * p.h_kv + it.kvh) * p.block_size + off) * ROW + c * 8 * Tile::ES;
-        const uint8_t* stage = &sm.t.newrow[wave][is_v ? 1 : 0][c * 8 * Tile::ES];
-        uint8_t* cache = (is_v ? p.v_store : p.k_store) + dst;
-        if constexpr (KV == kFP8) {
-          store8<kFP8>(cache, load8<kFP8>(stage));
-        } else {
-          store8<KV>(cache, load8<KV>(stage));
-        }
+        new_rows = load8<KV>(&sm.t.newrow[wave][is_v ? 1 : 0][c * 8 * Tile::ES]);
+        new_dst = (is_v ? p.v_store : p.k_store) + dst;
       }
     }
 
@@ -1532,6 +1531,9 @@ decode_mfma_kernel(Params p) {
       }
       __syncthreads();
       finish<D, MT, RT, !BAL>(p, it, k, sm.merge);
+    }
+    if constexpr (AP) {
+      if (new_dst != nullptr) store8<KV>(new_dst, new_rows);
     }
   };
 
