@@ -60,21 +60,21 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-step", 1): 161783871,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825", 1): 161358848,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-multi4", 1): 168376320,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-b32-step", 1): 161744967,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-b32", 1): 161319936,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa70b-bf16-47x825-b32-multi4", 1): 168337408,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa8b-bf16-256xU4096-step", 1): 2132165439,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa8b-bf16-256xU4096", 1): 2130027520,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "gqa8b-bf16-256xU4096-multi4", 1): 2148932635,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "mha-f16-64x4096-step", 1): 4299381783,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "mha-f16-64x4096", 1): 4297233408,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "mha-f16-64x4096-multi4", 1): 4301995008,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "fp8-prefix-32xU32768-step", 2): 1267016293,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "fp8-prefix-32xU32768", 2): 1268252169,
-    ("5ea1404cfe198215c0123c7817d22cf767f71485184f3715420fcae1c4c2bfae", "fp8-prefix-32xU32768-multi4", 2): 1290844314,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-step", 1): 161785920,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825", 1): 161361920,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-multi4", 1): 168400896,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-b32-step", 1): 161747012,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-b32", 1): 161323008,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-b32-multi4", 1): 168361984,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa8b-bf16-256xU4096-step", 1): 2132160426,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa8b-bf16-256xU4096", 1): 2130032644,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa8b-bf16-256xU4096-multi4", 1): 2148940810,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "mha-f16-64x4096-step", 1): 4299399579,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "mha-f16-64x4096", 1): 4297254912,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "mha-f16-64x4096-multi4", 1): 4301980672,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "fp8-prefix-32xU32768-step", 2): 1266974670,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "fp8-prefix-32xU32768", 2): 1267404824,
+    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "fp8-prefix-32xU32768-multi4", 2): 1290370932,
 }
 
 
