@@ -817,6 +817,10 @@ __device__ __forceinline__ uint32_t kv_load4(__amdgpu_buffer_rsrc_t r, int lane_
 // tiles take longer); past the best share the lone workgroups end last, and
 // the time grows fast, so the line below stays at or under it.
 constexpr int kPaceMinTiles = 8 * kDecodeWaves;
+// A step counts for at most this many ticks of the 100 MHz counter (10 us,
+// about 7 times a step of the 70B-style layer), so that a wave held up for
+// long (preempted, say) does not sleep in proportion.
+constexpr uint64_t kPaceMaxStepTicks = 1000;
 __host__ __device__ constexpr int pace_share32(int shared_cus, int row_tiles) {
   return (row_tiles == 2 ? 26 : 32) + (shared_cus > 16 ? (shared_cus - 16) / 7 : 0);
 }
@@ -1483,7 +1487,8 @@ decode_mfma_kernel(Params p) {
             const uint64_t now = __builtin_amdgcn_s_memrealtime();
             // no wait after the wave's last tile: only its merge is left
             if (t_step != 0 && c0 + i + b + 1 < n_my) {
-              const uint64_t until = now + (now - t_step) * (uint64_t)p.pace_share32 / 32;
+              const uint64_t step = now - t_step < kPaceMaxStepTicks ? now - t_step : kPaceMaxStepTicks;
+              const uint64_t until = now + step * (uint64_t)p.pace_share32 / 32;
               uint64_t t = now;
               while (t < until) {
                 __builtin_amdgcn_s_sleep(2);
