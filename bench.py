@@ -60,21 +60,21 @@ MULTI_TOKENS = 4
 # (kernel_source_sha256) and the workload / split count they ran.
 MEASURED_TRAFFIC = {
     # (kernel source sha256, workload, num_splits): bytes per launch
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-step", 1): 161785920,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825", 1): 161361920,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-multi4", 1): 168400896,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-b32-step", 1): 161747012,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-b32", 1): 161323008,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa70b-bf16-47x825-b32-multi4", 1): 168361984,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa8b-bf16-256xU4096-step", 1): 2132160426,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa8b-bf16-256xU4096", 1): 2130032644,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "gqa8b-bf16-256xU4096-multi4", 1): 2148940810,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "mha-f16-64x4096-step", 1): 4299399579,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "mha-f16-64x4096", 1): 4297254912,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "mha-f16-64x4096-multi4", 1): 4301980672,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "fp8-prefix-32xU32768-step", 2): 1266974670,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "fp8-prefix-32xU32768", 2): 1267404824,
-    ("28826a49fa63e67fd1e1e131b5f5e011d6130aef7170cea697b73d3d5740792b", "fp8-prefix-32xU32768-multi4", 2): 1290370932,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa70b-bf16-47x825-step", 1): 161785926,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa70b-bf16-47x825", 1): 161361920,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa70b-bf16-47x825-multi4", 1): 168399872,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa70b-bf16-47x825-b32-step", 1): 161747006,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa70b-bf16-47x825-b32", 1): 161323008,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa70b-bf16-47x825-b32-multi4", 1): 168360960,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa8b-bf16-256xU4096-step", 1): 2132160432,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa8b-bf16-256xU4096", 1): 2130032641,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "gqa8b-bf16-256xU4096-multi4", 1): 2148940803,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "mha-f16-64x4096-step", 1): 4299399281,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "mha-f16-64x4096", 1): 4297254912,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "mha-f16-64x4096-multi4", 1): 4301980672,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "fp8-prefix-32xU32768-step", 2): 1267052557,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "fp8-prefix-32xU32768", 2): 1267417925,
+    ("8103bae41d746a887ca72f3e4108a73f5914051d8b08feff7eb81f5cf33815b4", "fp8-prefix-32xU32768-multi4", 2): 1290396874,
 }
 
 
