@@ -45,6 +45,11 @@
 //   three workgroups per CU, the tiles come straight into a per-wave ring in
 //   LDS (buffer loads to LDS, waits placed by the kernel) instead of through
 //   registers.
+//   Pacing: when a grid that fits on the GPU at once leaves some CUs with one
+//   workgroup and others with two, the lone workgroups wait after each tile
+//   (short sleeps on the real-time counter, for a share of the tile's step
+//   time that grows with the number of shared CUs), so that the CUs holding
+//   two get HBM sooner and all end together.
 //
 // Matrix-core path (16-bit or FP8 caches, block_size 16 x 2^k)
 //   Scores: S^T[token][g] = K[token][:] . Q[g][:] with v_mfma_f32_16x16x32
