@@ -73,7 +73,11 @@ struct DecodeLaunch {
   // many, the dispatcher puts workgroups 0 .. kComputeUnits - 1 on CUs of
   // their own and the rest beside the first ones, so workgroups grid -
   // kComputeUnits .. kComputeUnits - 1 have a CU to themselves.  Those
-  // pace their tiles, leaving HBM to the CUs that hold two workgroups.
+  // pace their tiles, leaving HBM to the CUs that hold two workgroups; the
+  // launch does so for grids of at most 1.5 times the CUs (at most half of
+  // them shared: beyond that pacing measured no gain) whose pairs hold at
+  // least 8 tiles per wave.  This flag says the call's kernel kind may be
+  // paced; the launch checks the rest.
   bool pace = false;
   // Counters region of the workspace, in int32 slots: 0 sizes it for this
   // call's units; a fixed capacity (the library's own workspace) keeps the
