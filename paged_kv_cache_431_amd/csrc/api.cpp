@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -20,6 +21,26 @@ namespace {
 constexpr int64_t kResidentWorkgroups = 256 * 2;
 
 bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
+
+// Compute units of the current device, queried once per device (0 if the
+// query fails).  Pacing rests on the dispatch placement and the shares
+// measured on a whole MI355X (pkv::kComputeUnits CUs): a device that reports
+// another count (a partition of the GPU, say) runs unpaced.
+int current_device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0: not queried yet
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cache[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -277,7 +298,7 @@ pkv_status run_attention(void* out, int out_dtype, const void* q, int q_dtype, c
                                              : -1;
   a.lds_ring = lds_ring_fits(matrix_core, balanced, kv_dtype, head_dim, multi, row_tiles) &&
                decode_grid(num_seqs, h_kv, row_groups, n) > (int64_t)pkv::kComputeUnits * pkv::kDecodeWavesPerSimd;
-  a.pace = matrix_core && balanced == 0;
+  a.pace = matrix_core && balanced == 0 && current_device_cus() == pkv::kComputeUnits;
   const hipError_t e = pkv::launch_decode(a, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

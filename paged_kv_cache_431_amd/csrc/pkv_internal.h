@@ -19,7 +19,8 @@ constexpr int kDecodeWavesPerSimd = 3;
 // in LDS), and ranges of at least this many 16-token tiles.
 constexpr int kBalancedMaxSeqs = 1024;
 constexpr int kBalancedMinRange = 64;
-// Compute units of an MI355X.
+// Compute units of an MI355X (the work-split models assume a whole GPU;
+// pacing checks that the device reports this many).
 constexpr int kComputeUnits = 256;
 // Longest pairs first (decode grids that do not fit on the GPU at once): at
 // most this many sequences, ranked by tile count in this many bins (LDS).
