@@ -8,7 +8,9 @@ compute.  The cases are 40 sequences x 8 KV heads (320 workgroups, the
 paced beside paced ones, empty sequences, and lengths that leave the four
 waves of a workgroup unequal tile counts.  Decode, the one-launch step and
 several new query tokens (up to 4 tokens of 8 query heads: two row tiles,
-held by one workgroup) are paced.  Checks:
+held by one workgroup) are paced, and so is a grid that forced splits bring
+into the window (20 sequences x 8 KV heads x 2 splits), whose partial states
+are merged across workgroups.  Checks:
   * every output row against the oracle;
   * the output bit-equal to the same sequences run in a grid below the
     window (the first 30 sequences: 240 workgroups, none paced);
@@ -118,3 +120,47 @@ def test_paced_several_query_tokens(types):
                                   k_scale=c.t.k_scale, v_scale=c.t.v_scale, num_splits=1)
     torch.cuda.synchronize()
     assert torch.equal(sub, out[:rows]), f"{wl.name}: paced rows differ from the unpaced launch"
+
+
+@pytest.mark.parametrize("types", TYPES, ids=lambda t: "-".join(t))
+def test_paced_forced_splits(types):
+    """20 sequences x 8 KV heads x 2 forced splits: 320 workgroups, paced,
+    with partial states merged across workgroups (the last split of each
+    pair merges).  Decode against the oracle on every row and bit-equal to
+    the same sequences in an unpaced grid (the first 12: 192 workgroups);
+    the one-launch step bit-equal to scatter + decode."""
+    q, kv, new = types
+    rng = np.random.default_rng(97)
+    ctx = [int(c) for c in rng.integers(1500, 4001, size=20)]
+    ctx[3], ctx[8] = 0, 17  # an empty sequence and one too short to pace
+    wl = workloads.Workload(f"paced-splits-{q}-{kv}", 20, H_Q, H_KV, D, BS, q, kv, new, 97, contexts=tuple(ctx),
+                            extra_blocks=9)
+    print(f"[case] {wl.name} decode splits=2", flush=True)
+    c = Case(wl)
+    c.scatter()
+    out = c.decode(num_splits=2)
+    torch.cuda.synchronize()
+    assert_close(out, c.oracle_decode(), wl.kv_dtype, label=f"{wl.name} all rows")
+    sub = torch.empty((12, H_Q, D), dtype=torch.float32, device="cuda")
+    ws = pkv.make_workspace(12, H_Q, H_KV, D, BS, c.plan.max_context_len, 2)
+    pkv.pkv_paged_attention_decode(sub, c.t.q[:12].contiguous(), c.t.k_cache, c.t.v_cache,
+                                   c.block_tables[:12].contiguous(), c.context_lens[:12].contiguous(),
+                                   max_context_len=c.plan.max_context_len, k_scale=c.t.k_scale,
+                                   v_scale=c.t.v_scale, num_splits=2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sub, out[:12]), f"{wl.name}: paced rows differ from the unpaced launch"
+
+    print(f"[case] {wl.name} step splits=2", flush=True)
+    two = Case(wl)
+    two.scatter()
+    ref_out = two.decode(num_splits=2)
+    torch.cuda.synchronize()
+    one = Case(wl)
+    step_out = torch.empty_like(ref_out)
+    pkv.pkv_decode_step(step_out, one.t.q, one.t.new_k, one.t.new_v, one.t.k_cache, one.t.v_cache, one.block_tables,
+                        one.context_lens, max_context_len=one.plan.max_context_len, k_scale=one.t.k_scale,
+                        v_scale=one.t.v_scale, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(step_out, ref_out), f"{wl.name}: step output differs from scatter + decode"
+    assert torch.equal(one.t.k_cache.view(torch.uint8), two.t.k_cache.view(torch.uint8)), f"{wl.name}: K pool"
+    assert torch.equal(one.t.v_cache.view(torch.uint8), two.t.v_cache.view(torch.uint8)), f"{wl.name}: V pool"
